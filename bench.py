@@ -1,0 +1,252 @@
+"""Benchmark of grouped shared-prefix attention (fwd + bwd) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--no-baseline] [--no-cpu] [--cpu-seconds S]
+
+One step is one pass of the whole path over one packed batch with inputs
+already resident in HBM: pg_pack (plan + descriptor upload), pg_attn_fwd and
+pg_attn_bwd.  Prints ONE JSON line on stdout; progress goes to stderr.
+
+value      effective TFLOP/s = 14 * d * Hq * pairs / step time, where pairs is
+           the number of unmasked (query, key) pairs per head of the grouped
+           layout (forward 4d, backward 10d per pair: the flash-attention
+           convention; masked work and recomputation are not credited).
+roofline   the kernel with the largest share of the step, timed with HIP
+           events recorded by the library on the stream it launches on.
+cpu_baseline  the fp64 oracle (repeated-prefix baseline) on a bounded sample
+           of the same workload, on this host's cores, credited with the same
+           effective-FLOP formula for the rows it covered.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+METRIC = "grouped-attn fwd+bwd TFLOP/s & % MFMA peak; speedup vs repeated-prefix"
+
+# algorithmic flops per unmasked (query, key) pair and query head, per kernel
+KERNEL_FLOPS_PER_PAIR_D = {"fwd": 4, "bwd_dkdv": 8, "bwd_dq": 6}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="bf16_gqa_g16_p8192")
+    ap.add_argument("--no-baseline", action="store_true", help="skip the repeated-prefix run")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="approximate CPU time budget of the oracle sample")
+    return ap.parse_args(argv)
+
+
+def groups_of(w):
+    return [(g.prefix_len, list(g.resp_lens)) for g in w.groups]
+
+
+class Runner:
+    """Holds device inputs/outputs for one layout and runs steps through the C ABI."""
+
+    def __init__(self, pg, torch, groups, w, tensors):
+        self.pg, self.torch, self.groups, self.w = pg, torch, groups, w
+        self.q, self.k, self.v, self.do = tensors
+        self.batch = pg.pg_pack(groups, w.num_q_heads, w.num_kv_heads, w.head_dim)
+        T = self.batch.total_rows
+        dev = self.q.device
+        self.o = torch.empty_like(self.q)
+        self.lse = torch.empty((w.num_q_heads, T), dtype=torch.float32, device=dev)
+        self.dq = torch.empty_like(self.q)
+        self.dk = torch.empty_like(self.k)
+        self.dv = torch.empty_like(self.v)
+        code = pg.PG_BF16 if self.q.dtype == torch.bfloat16 else pg.PG_F32
+        ws = pg.lib().pg_attn_bwd_workspace_size(ctypes.byref(self.batch.desc), code)
+        self.ws = torch.empty(ws, dtype=torch.uint8, device=dev)
+
+    def step(self):
+        pg = self.pg
+        w = self.w
+        self.batch = pg.pg_pack(self.groups, w.num_q_heads, w.num_kv_heads, w.head_dim)
+        pg.pg_attn_fwd(self.batch, self.q, self.k, self.v, None, out=self.o, lse=self.lse)
+        pg.pg_attn_bwd(self.batch, self.q, self.k, self.v, self.o, self.lse, self.do, None,
+                       dq=self.dq, dk=self.dk, dv=self.dv, workspace=self.ws)
+
+    def timed(self, steps, warmup):
+        torch = self.torch
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        self.pg.pg_kernel_timing(True)
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        start.record()
+        for _ in range(steps):
+            self.step()
+        stop.record()
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) * 1e3
+        kernels = self.pg.pg_kernel_times()
+        self.pg.pg_kernel_timing(False)
+        return start.elapsed_time(stop) / steps, wall / steps, kernels
+
+
+def cpu_baseline(w, arrs, budget_s):
+    """The oracle as it stands, on kv head 0 and the first members of group 0."""
+    from oracle.attention import pair_counts, repeated_prefix_attention
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        threads = 1
+    P, rs = w.groups[0].prefix_len, list(w.groups[0].resp_lens)
+    rep = w.num_q_heads // w.num_kv_heads
+    done, elapsed = [], 0.0
+    for i, r in enumerate(rs):
+        s = P + sum(rs[:i])
+        rows = np.concatenate([np.arange(P), np.arange(s, s + r)])
+        sub = {k: v[rows] for k, v in arrs.items()}
+        t0 = time.perf_counter()
+        repeated_prefix_attention([(P, [r])], sub["q"], sub["k"], sub["v"], sub["do"], kv_heads=[0])
+        elapsed += time.perf_counter() - t0
+        done.append(r)
+        log(f"[bench] cpu oracle: member {i} (P={P}, R={r}) done, {elapsed:.1f}s")
+        if elapsed >= budget_s:
+            break
+    pairs, _ = pair_counts([(P, done)])
+    flops = 14.0 * w.head_dim * rep * pairs
+    return {
+        "value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"fp64 repeated-prefix oracle, kv head 0 ({rep} query heads), group 0 prefix "
+                   f"P={P} with its first {len(done)} responses {done}; {elapsed:.1f} s; credited "
+                   f"14*d*heads*pairs of that grouped sub-batch ({pairs} pairs)"),
+        "seconds": elapsed,
+    }
+
+
+def main(argv=None) -> int:
+    a = parse(argv)
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported "
+              "(the path shards across GPUs by group or kv head; not built here)", file=sys.stderr)
+        return 2
+    import torch
+    import shared_prefix_grouped_amd as pg
+    from workloads import attention_workloads, draw_attention_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    pg.lib()  # fails loudly when the HIP library is not built
+    w = attention_workloads()[a.workload]
+    groups = groups_of(w)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    log(f"[bench] workload {w.name}: {w.description}; T={w.total_rows}")
+    t0 = time.perf_counter()
+    arrs = draw_attention_inputs(w)
+    tens = [torch.from_numpy(arrs[n]).to("cuda").to(dt) for n in ("q", "k", "v", "do")]
+    torch.cuda.synchronize()
+    log(f"[bench] inputs on device in {time.perf_counter() - t0:.1f}s")
+
+    run = Runner(pg, torch, groups, w, tens)
+    pairs, base_pairs = run.batch.pairs, run.batch.baseline_pairs
+    eff_flops = 14.0 * w.head_dim * w.num_q_heads * pairs
+    ms, wall_ms, kern = run.timed(a.steps, a.warmup)
+    value = eff_flops / (ms * 1e-3) / 1e12
+    log(f"[bench] grouped: {ms:.3f} ms/step (host wall {wall_ms:.3f}), {value:.1f} TFLOP/s; "
+        f"kernels {kern}")
+
+    # dominant kernel roofline
+    per_launch = {n: (ms_tot / cnt if cnt else 0.0) for n, (cnt, ms_tot) in kern.items()}
+    dom = max(per_launch, key=per_launch.get)
+    T, hq, d = w.total_rows, w.num_q_heads, w.head_dim
+    esz = 2 if w.dtype == "bf16" else 4
+    if dom in KERNEL_FLOPS_PER_PAIR_D:
+        alg = KERNEL_FLOPS_PER_PAIR_D[dom] * d * hq * pairs
+        achieved = alg / (per_launch[dom] * 1e-3) / 1e12
+        peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+        roof = {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": peak,
+                "unit": "TFLOP/s", "frac": achieved / peak, "traffic": None,
+                "algorithmic_flop_per_launch": alg, "avg_launch_ms": per_launch[dom]}
+    else:
+        alg = 2 * T * hq * d * esz + T * hq * 4
+        achieved = alg / (per_launch[dom] * 1e-3) / 1e9
+        roof = {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS, "traffic": None,
+                "algorithmic_bytes_per_launch": alg, "avg_launch_ms": per_launch[dom]}
+
+    speed = None
+    base_ms = None
+    if not a.no_baseline:
+        # same kernels on the repeated-prefix layout: every [P; R_i] as its own group
+        idx, bgroups, t = [], [], 0
+        for P, rs in groups:
+            s = t + P
+            for r in rs:
+                idx.append(np.concatenate([np.arange(t, t + P), np.arange(s, s + r)]))
+                bgroups.append((P, [r]))
+                s += r
+            t = s
+        idx_t = torch.from_numpy(np.concatenate(idx)).to("cuda")
+        btens = [x.index_select(0, idx_t).contiguous() for x in tens]
+        brun = Runner(pg, torch, bgroups, w, btens)
+        bsteps = max(2, a.steps // 4)
+        base_ms, _, _ = brun.timed(bsteps, 1)
+        speed = base_ms / ms
+        log(f"[bench] repeated-prefix layout: {base_ms:.3f} ms/step over {bsteps} steps; "
+            f"speedup {speed:.2f}x (ideal {base_pairs / pairs:.2f}x)")
+        del brun, btens
+
+    cpu = None
+    if not a.no_cpu:
+        cpu = cpu_baseline(w, arrs, a.cpu_seconds)
+        log(f"[bench] cpu baseline {cpu['value']:.4f} TFLOP/s on {cpu['cores']} threads")
+
+    G = sum(len(rs) for _, rs in groups)
+    res = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic (seeded N(0,1) inputs, packed varlen layout)",
+        "config": {"workload": w.name, "groups": [[P, rs] for P, rs in groups],
+                   "num_q_heads": hq, "num_kv_heads": w.num_kv_heads, "head_dim": d,
+                   "total_rows": T, "pairs_per_head": pairs, "baseline_pairs_per_head": base_pairs,
+                   "effective_flop_per_step": eff_flops, "step": "pg_pack + pg_attn_fwd + pg_attn_bwd"},
+        "pct_mfma_peak": round(100.0 * value / (PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS), 2),
+        "speedup_vs_repeated_prefix": None if speed is None else round(speed, 3),
+        "repeated_prefix_ms_per_step": None if base_ms is None else round(base_ms, 4),
+        "ideal_speedup_pairs": round(base_pairs / pairs, 3),
+        "kernels_ms_per_launch": {n: round(v, 4) for n, v in per_launch.items() if v},
+        "host_wall_ms_per_step": round(wall_ms, 4),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "context": "pages: prefix cost tends to 1/G of the baseline as P/R grows; 'up to 8x' for "
+                   "long contexts (no hardware stated)",
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

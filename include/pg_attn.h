@@ -1,0 +1,217 @@
+/*
+ * pg_attn.h -- C ABI of the grouped shared-prefix attention library (libpg_attn.so).
+ *
+ * The operation (web pages on "Prefix Grouper: Efficient GRPO Training through
+ * Shared-Prefix Forward"; the Pith review on pith.science, sections "What
+ * carries the argument" and "Core claim"; the skillsmp.com page
+ * "prefix-grouper-grpo", sections "Core Concept" and "Step 3: Restructure
+ * Input Format"):
+ *
+ *   A group is one shared prefix P followed by G responses, packed as the rows
+ *   [P; R_1; ...; R_G]; a batch packs groups one after another, without padding.
+ *   Attention is split in two: causal self-attention over the prefix rows,
+ *   computed once per group, and a suffix pass in which the queries of
+ *   response i attend to every prefix key and to the keys of response i up to
+ *   themselves, never to another response.  Every row therefore sees exactly
+ *   the causal context it has in the repeated-prefix baseline [P; R_i], and
+ *   the outputs and gradients equal the baseline's; the gradient of a shared
+ *   prefix row is the sum of the gradients of its G copies (Lemma 2.1).
+ *
+ *   Equivalently, with packed row indices, query row q of a group starting at
+ *   row g0 with prefix end row pe sees key row k iff
+ *       g0 <= k <= q  and  (k < pe  or  k >= start of q's response).
+ *
+ * Conventions
+ *   - Rows: T packed rows.  Q, O, dQ, dO are [T, Hq, d]; K, V, dK, dV are
+ *     [T, Hkv, d]; row-major, d contiguous, no padding between rows or heads.
+ *   - LSE is float [Hq, T]: natural-log logsumexp of the scaled scores of
+ *     each (head, row).
+ *   - Grouped-query attention: query head h uses key/value head
+ *     h / (Hq / Hkv).  Hq must be a multiple of Hkv.
+ *   - Element type: PG_BF16 (bfloat16 storage, float32 accumulation) or
+ *     PG_F32 (float32 throughout).  Outputs are in the input type, rounded to
+ *     nearest even from float32.  head_dim 64 or 128.
+ *   - Device pointers must be 16-byte aligned.  All device buffers are
+ *     allocated and owned by the caller; the library never allocates device
+ *     memory.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Kernels are
+ *     enqueued on it; the call returns before they finish.
+ *   - Results are bitwise reproducible for the same inputs, descriptor and
+ *     device: no floating-point atomics, every reduction has a fixed order.
+ *
+ * Errors
+ *   Every call validates its arguments on the host before enqueuing anything
+ *   and returns a pg_status.  PG_ERR_INVALID_ARG: bad lengths, null or
+ *   misaligned pointers, inconsistent descriptor.  PG_ERR_UNSUPPORTED: a
+ *   head_dim or dtype the kernels do not implement.  PG_ERR_WORKSPACE: a
+ *   buffer smaller than the size function reports.  PG_ERR_HIP: a HIP runtime
+ *   call or a launch failed.  pg_last_error() returns a message for the last
+ *   non-OK status of the calling thread.  Faults inside kernels surface at the
+ *   caller's next synchronisation.  No call aborts the process and no C++
+ *   exception crosses this interface.
+ */
+#ifndef PG_ATTN_H
+#define PG_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PG_OK = 0,
+  PG_ERR_INVALID_ARG = 1,
+  PG_ERR_UNSUPPORTED = 2,
+  PG_ERR_WORKSPACE = 3,
+  PG_ERR_HIP = 4
+} pg_status;
+
+typedef enum { PG_F32 = 0, PG_BF16 = 1 } pg_dtype;
+
+/* Row tiles of the work lists built by pg_pack (fixed by the library build). */
+#define PG_TILE_Q 128  /* query rows per forward / dQ work item */
+#define PG_TILE_KV 128 /* key rows per dK/dV work item */
+
+/* Host description of a packed batch (input of pg_pack).  All arrays are
+ * host memory, read during the call only.
+ *   num_groups  >= 0
+ *   prefix_len  [num_groups], each >= 0
+ *   num_resp    [num_groups], each >= 1 (G of the group)
+ *   resp_len    [sum(num_resp)], each >= 0, group-major (group 0's responses
+ *               first, in packed order)
+ * The total row count T = sum(prefix_len) + sum(resp_len) must fit int32. */
+typedef struct {
+  int32_t num_groups;
+  const int32_t *prefix_len;
+  const int32_t *num_resp;
+  const int32_t *resp_len;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+} pg_groups;
+
+/* Descriptor filled by pg_pack.  The pointer members address the caller's
+ * buffer passed to pg_pack (device memory for pg_pack, host memory for
+ * pg_pack_host) and stay valid as long as that buffer does.  Callers treat it
+ * as read-only; it is reused unchanged by pg_attn_fwd, pg_attn_bwd and
+ * pg_rope for every layer of the same batch.
+ *   row_lo[T]    first key row of the row's own segment: the group's first
+ *                row for a prefix row, the response's first row for a
+ *                response row.  A query row q sees key rows
+ *                [group start, prefix end) and [row_lo[q], q].
+ *   row_hi[T]    one past the last query row that sees key row k: the group's
+ *                end for a prefix row, the response's end for a response row.
+ *                Key row k is seen by exactly the query rows [k, row_hi[k]).
+ *   q_tiles      [num_q_tiles][4] = {q0, q1, group start, prefix end}: query
+ *                rows [q0, q1) of one group, q1 - q0 <= PG_TILE_Q, ordered by
+ *                decreasing cost.
+ *   kv_tiles     [num_kv_tiles][4] = {k0, k1, q_end, prefix end}: key rows
+ *                [k0, k1) of one group, k1 - k0 <= PG_TILE_KV, seen by query
+ *                rows inside [k0, q_end), ordered by decreasing cost.
+ *   group_start  [num_groups + 1], prefix_end [num_groups],
+ *   resp_start   [num_resp], resp_len [num_resp], resp_group [num_resp]:
+ *                the packed offsets, for callers.
+ *   pairs           unmasked (query, key) pairs per query head;
+ *   baseline_pairs  the same count for the repeated-prefix layout (each
+ *                   [P; R_i] on its own). */
+typedef struct {
+  int32_t num_groups, num_resp, total_rows;
+  int32_t num_q_heads, num_kv_heads, head_dim;
+  int32_t num_q_tiles, num_kv_tiles;
+  int64_t pairs, baseline_pairs;
+  const int32_t *row_lo;
+  const int32_t *row_hi;
+  const int32_t *q_tiles;
+  const int32_t *kv_tiles;
+  const int32_t *group_start;
+  const int32_t *prefix_end;
+  const int32_t *resp_start;
+  const int32_t *resp_len;
+  const int32_t *resp_group;
+  size_t buf_bytes; /* bytes of the buffer actually used */
+} pg_desc;
+
+/* Bytes pg_pack needs in its device buffer for this batch; 0 if the
+ * description is invalid (then pg_last_error() says why). */
+size_t pg_pack_buffer_size(const pg_groups *g);
+
+/* Plan a packed batch: validate the lengths, build row_lo/row_hi, the tile
+ * work lists and the offsets, and copy them to the device buffer `d_buf`
+ * (>= pg_pack_buffer_size bytes, 16-byte aligned).  If `d_pos_ids` is not
+ * NULL it receives int32 [T] position ids as in the repeated-prefix baseline:
+ * prefix row t of a group -> t, row j of a response -> P + j (Pith review,
+ * "What carries the argument").  The copy is synchronous with respect to the
+ * host: host arrays may be freed when the call returns; it is ordered on
+ * `stream`.  Fills *out. */
+pg_status pg_pack(const pg_groups *g, void *d_buf, size_t buf_bytes, int32_t *d_pos_ids,
+                  pg_desc *out, void *stream);
+
+/* Same plan as pg_pack, written to host memory (no GPU involved); the
+ * pointers in *out address `h_buf`.  For inspection and tests. */
+pg_status pg_pack_host(const pg_groups *g, void *h_buf, size_t buf_bytes, int32_t *h_pos_ids,
+                       pg_desc *out);
+
+/* Forward: O = grouped attention(Q, K, V) and LSE, for every packed row and
+ * query head.  softmax_scale <= 0 selects 1/sqrt(head_dim).  Prefix rows are
+ * computed once per group (prefix-only causal attention); response rows
+ * attend to the prefix and their own response (Pith review, "What carries the
+ * argument").  q, k, v: input, o: output [T,Hq,d], lse: output float [Hq,T]. */
+pg_status pg_attn_fwd(const pg_desc *d, pg_dtype t, float softmax_scale, const void *q,
+                      const void *k, const void *v, void *o, float *lse, void *stream);
+
+/* Bytes of scratch pg_attn_bwd needs: float [Hq, T] for rowsum(dO * O). */
+size_t pg_attn_bwd_workspace_size(const pg_desc *d, pg_dtype t);
+
+/* Backward: gradients of sum(O * dO) with respect to Q, K, V, recomputing the
+ * softmax from the saved LSE.  dK and dV of a prefix row are summed over the
+ * query rows of the prefix and of all G responses of its group and over the
+ * query heads sharing its key/value head, in a fixed order (Pith review,
+ * "Core claim", Lemma 2.1).  Inputs q, k, v, o, lse, dout as produced by /
+ * given to pg_attn_fwd; outputs dq [T,Hq,d], dk, dv [T,Hkv,d] are fully
+ * overwritten.  `workspace` is device scratch of at least
+ * pg_attn_bwd_workspace_size bytes (contents need not be initialised). */
+pg_status pg_attn_bwd(const pg_desc *d, pg_dtype t, float softmax_scale, const void *q,
+                      const void *k, const void *v, const void *o, const float *lse,
+                      const void *dout, void *dq, void *dk, void *dv, void *workspace,
+                      size_t ws_bytes, void *stream);
+
+/* Rotary position embedding at the baseline position ids, in place on x
+ * [T, num_heads, head_dim] (PG_BF16 or PG_F32, rotate-half pairing: element i
+ * with element i + d/2, angle pos * theta^(-2i/d)), computed in float32.
+ * pos_ids: int32 [T] from pg_pack.  inverse != 0 applies the transposed
+ * rotation (the backward of the forward rotation).  Response row j of a group
+ * is rotated as position P + j, so relative offsets match the baseline [P; R_i]
+ * (Pith review, "What carries the argument" and "Load-bearing premise"). */
+pg_status pg_rope(const pg_desc *d, pg_dtype t, void *x, int32_t num_heads, int32_t head_dim,
+                  const int32_t *pos_ids, float theta, int32_t inverse, void *stream);
+
+/* Kernel timing for benchmarks.  While enabled, every kernel the library
+ * launches is bracketed by two HIP events recorded on the stream it is
+ * launched on.  pg_kernel_timing(1) clears the counters and enables,
+ * pg_kernel_timing(0) disables.  pg_kernel_times waits for the recorded events
+ * and returns the number of launches and their total duration in milliseconds
+ * for one kernel id (PG_KERNEL_*); it fails with PG_ERR_INVALID_ARG for an
+ * unknown id.  pg_kernel_name returns the kernel's name, or NULL.  Not
+ * thread-safe with respect to concurrent enabling/reading. */
+#define PG_KERNEL_FWD 0
+#define PG_KERNEL_BWD_PRE 1
+#define PG_KERNEL_BWD_DKDV 2
+#define PG_KERNEL_BWD_DQ 3
+#define PG_KERNEL_ROPE 4
+#define PG_KERNEL_COUNT 5
+pg_status pg_kernel_timing(int32_t enable);
+pg_status pg_kernel_times(int32_t kernel_id, int64_t *launches, double *total_ms);
+const char *pg_kernel_name(int32_t kernel_id);
+
+/* Message for the last non-OK status returned on the calling thread. */
+const char *pg_last_error(void);
+
+/* Library version string. */
+const char *pg_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PG_ATTN_H */

@@ -1,0 +1,514 @@
+// Host side of libpg_attn: argument validation, the packed-batch planner
+// (pg_pack) and kernel launches.  See include/pg_attn.h for the contract.
+//
+// The planner turns per-group lengths into the packed row layout
+// [P; R_1; ...; R_G] (skillsmp.com "prefix-grouper-grpo", "Step 3: Restructure
+// Input Format", here without padding) and into per-row visibility bounds:
+// query row q sees key rows [group start, prefix end) and [row_lo[q], q]
+// (Pith review of Prefix Grouper, "What carries the argument": a response
+// token sees the whole prefix and its own response up to itself).
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <mutex>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "pg_attn.h"
+#include "pg_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+pg_status fail(pg_status st, const std::string &msg) {
+  g_last_error = msg;
+  return st;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t align16(size_t x) { return (x + 15) & ~size_t(15); }
+
+// Byte offsets of each array inside the descriptor buffer.
+struct Layout {
+  size_t row_lo, row_hi, q_tiles, kv_tiles, group_start, prefix_end, resp_start, resp_len,
+      resp_group, total;
+};
+
+Layout make_layout(int64_t T, int64_t n_groups, int64_t n_resp, int64_t n_qt, int64_t n_kvt) {
+  Layout L{};
+  size_t off = 0;
+  auto take = [&](size_t &field, int64_t n_int32) {
+    field = off;
+    off = align16(off + size_t(n_int32) * 4);
+  };
+  take(L.row_lo, T);
+  take(L.row_hi, T);
+  take(L.q_tiles, 4 * n_qt);
+  take(L.kv_tiles, 4 * n_kvt);
+  take(L.group_start, n_groups + 1);
+  take(L.prefix_end, n_groups);
+  take(L.resp_start, n_resp);
+  take(L.resp_len, n_resp);
+  take(L.resp_group, n_resp);
+  L.total = std::max<size_t>(off, 16);
+  return L;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Validate a pg_groups and compute the sizes that do not need the full plan.
+pg_status check_groups(const pg_groups *g, int64_t *T_out, int64_t *n_resp_out,
+                       int64_t *n_qt_out, int64_t *n_kvt_out) {
+  if (!g) return fail(PG_ERR_INVALID_ARG, "pg_groups is NULL");
+  if (g->num_groups < 0) return fail(PG_ERR_INVALID_ARG, "num_groups < 0");
+  if (g->num_groups > 0 && (!g->prefix_len || !g->num_resp || !g->resp_len))
+    return fail(PG_ERR_INVALID_ARG, "prefix_len, num_resp and resp_len must not be NULL");
+  if (g->num_q_heads <= 0 || g->num_kv_heads <= 0)
+    return fail(PG_ERR_INVALID_ARG, "head counts must be positive");
+  if (g->num_q_heads % g->num_kv_heads)
+    return fail(PG_ERR_INVALID_ARG, "num_q_heads must be a multiple of num_kv_heads");
+  if (g->head_dim != 64 && g->head_dim != 128)
+    return fail(PG_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  int64_t T = 0, n_resp = 0, n_qt = 0, n_kvt = 0;
+  for (int32_t i = 0; i < g->num_groups; ++i) {
+    if (g->prefix_len[i] < 0) return fail(PG_ERR_INVALID_ARG, "prefix_len < 0 in group " + std::to_string(i));
+    if (g->num_resp[i] < 1) return fail(PG_ERR_INVALID_ARG, "num_resp < 1 in group " + std::to_string(i));
+    int64_t rows = g->prefix_len[i];
+    for (int32_t r = 0; r < g->num_resp[i]; ++r) {
+      int32_t len = g->resp_len[n_resp + r];
+      if (len < 0) return fail(PG_ERR_INVALID_ARG, "resp_len < 0 in group " + std::to_string(i));
+      rows += len;
+    }
+    n_resp += g->num_resp[i];
+    T += rows;
+    if (T > INT32_MAX / 2) return fail(PG_ERR_INVALID_ARG, "total rows exceed the int32 range");
+    n_qt += ceil_div(rows, PG_TILE_Q);
+    n_kvt += ceil_div(rows, PG_TILE_KV);
+  }
+  if (T * int64_t(g->num_q_heads) * g->head_dim > (int64_t(1) << 40))
+    return fail(PG_ERR_INVALID_ARG, "tensor too large");
+  *T_out = T;
+  *n_resp_out = n_resp;
+  *n_qt_out = n_qt;
+  *n_kvt_out = n_kvt;
+  return PG_OK;
+}
+
+struct Tile {
+  int32_t a, b, c, d;
+  int64_t cost;
+  int64_t order;
+};
+
+// Build the whole plan into `buf` (host memory of at least L.total bytes).
+pg_status build_plan(const pg_groups *g, char *buf, size_t buf_bytes, int32_t *pos_ids,
+                     pg_desc *out, Layout *L_out) {
+  int64_t T, n_resp, n_qt, n_kvt;
+  pg_status st = check_groups(g, &T, &n_resp, &n_qt, &n_kvt);
+  if (st != PG_OK) return st;
+  Layout L = make_layout(T, g->num_groups, n_resp, n_qt, n_kvt);
+  if (buf_bytes < L.total)
+    return fail(PG_ERR_WORKSPACE, "descriptor buffer too small: need " + std::to_string(L.total) +
+                                      " bytes, got " + std::to_string(buf_bytes));
+  std::memset(buf, 0, L.total);
+  auto arr = [&](size_t off) { return reinterpret_cast<int32_t *>(buf + off); };
+  int32_t *row_lo = arr(L.row_lo), *row_hi = arr(L.row_hi);
+  int32_t *gstart = arr(L.group_start), *pend = arr(L.prefix_end);
+  int32_t *rstart = arr(L.resp_start), *rlen = arr(L.resp_len), *rgroup = arr(L.resp_group);
+
+  std::vector<Tile> qt, kvt;
+  qt.reserve(n_qt);
+  kvt.reserve(n_kvt);
+  int64_t pairs = 0, base_pairs = 0;
+  int32_t t = 0, ri = 0;
+  for (int32_t gi = 0; gi < g->num_groups; ++gi) {
+    const int32_t P = g->prefix_len[gi];
+    const int32_t g0 = t, pe = t + P;
+    gstart[gi] = g0;
+    pend[gi] = pe;
+    int32_t gend = pe;
+    for (int32_t r = 0; r < g->num_resp[gi]; ++r) gend += g->resp_len[ri + r];
+    // prefix rows: own segment is the prefix itself; seen by every later row of the group
+    for (int32_t x = g0; x < pe; ++x) {
+      row_lo[x] = g0;
+      row_hi[x] = gend;
+      if (pos_ids) pos_ids[x] = x - g0;
+    }
+    pairs += int64_t(P) * (P + 1) / 2;
+    int32_t s = pe;
+    for (int32_t r = 0; r < g->num_resp[gi]; ++r, ++ri) {
+      const int32_t R = g->resp_len[ri];
+      rstart[ri] = s;
+      rlen[ri] = R;
+      rgroup[ri] = gi;
+      for (int32_t x = s; x < s + R; ++x) {
+        row_lo[x] = s;
+        row_hi[x] = s + R;
+        if (pos_ids) pos_ids[x] = P + (x - s);
+      }
+      pairs += int64_t(R) * P + int64_t(R) * (R + 1) / 2;
+      const int64_t Lb = int64_t(P) + R;
+      base_pairs += Lb * (Lb + 1) / 2;
+      s += R;
+    }
+    // query tiles: cost = number of visible keys summed over the tile's rows
+    for (int32_t q0 = g0; q0 < gend; q0 += PG_TILE_Q) {
+      const int32_t q1 = std::min(gend, q0 + PG_TILE_Q);
+      int64_t cost = 0;
+      for (int32_t x = q0; x < q1; ++x)
+        cost += (x < pe) ? (x - g0 + 1) : (int64_t(P) + (x - row_lo[x] + 1));
+      qt.push_back({q0, q1, g0, pe, cost, int64_t(qt.size())});
+    }
+    // key tiles: cost = number of query rows seeing each key, summed
+    for (int32_t k0 = g0; k0 < gend; k0 += PG_TILE_KV) {
+      const int32_t k1 = std::min(gend, k0 + PG_TILE_KV);
+      int64_t cost = 0;
+      int32_t qend = 0;
+      for (int32_t x = k0; x < k1; ++x) {
+        cost += row_hi[x] - x;
+        qend = std::max(qend, row_hi[x]);
+      }
+      kvt.push_back({k0, k1, qend, pe, cost, int64_t(kvt.size())});
+    }
+    t = gend;
+  }
+  gstart[g->num_groups] = t;
+  // longest-processing-time-first order; ties keep packed order
+  auto by_cost = [](const Tile &x, const Tile &y) {
+    return x.cost != y.cost ? x.cost > y.cost : x.order < y.order;
+  };
+  std::sort(qt.begin(), qt.end(), by_cost);
+  std::sort(kvt.begin(), kvt.end(), by_cost);
+  int32_t *qa = arr(L.q_tiles), *ka = arr(L.kv_tiles);
+  for (size_t i = 0; i < qt.size(); ++i) {
+    qa[4 * i + 0] = qt[i].a;
+    qa[4 * i + 1] = qt[i].b;
+    qa[4 * i + 2] = qt[i].c;
+    qa[4 * i + 3] = qt[i].d;
+  }
+  for (size_t i = 0; i < kvt.size(); ++i) {
+    ka[4 * i + 0] = kvt[i].a;
+    ka[4 * i + 1] = kvt[i].b;
+    ka[4 * i + 2] = kvt[i].c;
+    ka[4 * i + 3] = kvt[i].d;
+  }
+  pg_desc d{};
+  d.num_groups = g->num_groups;
+  d.num_resp = int32_t(n_resp);
+  d.total_rows = int32_t(T);
+  d.num_q_heads = g->num_q_heads;
+  d.num_kv_heads = g->num_kv_heads;
+  d.head_dim = g->head_dim;
+  d.num_q_tiles = int32_t(qt.size());
+  d.num_kv_tiles = int32_t(kvt.size());
+  d.pairs = pairs;
+  d.baseline_pairs = base_pairs;
+  d.buf_bytes = L.total;
+  *out = d;
+  *L_out = L;
+  return PG_OK;
+}
+
+void point_into(pg_desc *d, const Layout &L, const char *base) {
+  auto p = [&](size_t off) { return reinterpret_cast<const int32_t *>(base + off); };
+  d->row_lo = p(L.row_lo);
+  d->row_hi = p(L.row_hi);
+  d->q_tiles = p(L.q_tiles);
+  d->kv_tiles = p(L.kv_tiles);
+  d->group_start = p(L.group_start);
+  d->prefix_end = p(L.prefix_end);
+  d->resp_start = p(L.resp_start);
+  d->resp_len = p(L.resp_len);
+  d->resp_group = p(L.resp_group);
+}
+
+pg_status check_desc(const pg_desc *d) {
+  if (!d) return fail(PG_ERR_INVALID_ARG, "pg_desc is NULL");
+  if (d->total_rows < 0 || d->num_q_heads <= 0 || d->num_kv_heads <= 0 ||
+      d->num_q_heads % d->num_kv_heads || d->num_q_tiles < 0 || d->num_kv_tiles < 0)
+    return fail(PG_ERR_INVALID_ARG, "descriptor is not one filled by pg_pack");
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(PG_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (d->total_rows > 0 && (!d->row_lo || !d->row_hi || !d->q_tiles || !d->kv_tiles))
+    return fail(PG_ERR_INVALID_ARG, "descriptor arrays are NULL");
+  return PG_OK;
+}
+
+pg_status check_dtype(pg_dtype t) {
+  if (t != PG_F32 && t != PG_BF16) return fail(PG_ERR_UNSUPPORTED, "dtype must be PG_F32 or PG_BF16");
+  return PG_OK;
+}
+
+pg_status check_ptrs(std::initializer_list<std::pair<const void *, const char *>> ptrs) {
+  for (auto &pr : ptrs) {
+    if (!pr.first) return fail(PG_ERR_INVALID_ARG, std::string(pr.second) + " is NULL");
+    if (!aligned16(pr.first))
+      return fail(PG_ERR_INVALID_ARG, std::string(pr.second) + " is not 16-byte aligned");
+  }
+  return PG_OK;
+}
+
+pg::Plan plan_of(const pg_desc *d) {
+  pg::Plan p;
+  p.T = d->total_rows;
+  p.Hq = d->num_q_heads;
+  p.Hkv = d->num_kv_heads;
+  p.D = d->head_dim;
+  p.n_q_tiles = d->num_q_tiles;
+  p.n_kv_tiles = d->num_kv_tiles;
+  p.row_lo = d->row_lo;
+  p.row_hi = d->row_hi;
+  p.q_tiles = d->q_tiles;
+  p.kv_tiles = d->kv_tiles;
+  return p;
+}
+
+pg_status hip_status(hipError_t e, const char *what) {
+  if (e == hipSuccess) return PG_OK;
+  return fail(PG_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+float resolve_scale(float s, int D) { return s > 0.f ? s : 1.0f / std::sqrt(float(D)); }
+
+// ---------------------------------------------------------------- kernel timing
+const char *const kKernelNames[PG_KERNEL_COUNT] = {"fwd", "bwd_pre", "bwd_dkdv", "bwd_dq", "rope"};
+
+struct TimedLaunch {
+  int id;
+  hipEvent_t start, stop;
+};
+
+struct Timing {
+  std::mutex mu;
+  bool enabled = false;
+  std::vector<TimedLaunch> pending;
+  std::vector<hipEvent_t> pool;
+  int64_t launches[PG_KERNEL_COUNT] = {};
+  double total_ms[PG_KERNEL_COUNT] = {};
+};
+
+Timing &timing() {
+  static Timing t;
+  return t;
+}
+
+hipEvent_t take_event(Timing &t) {
+  if (!t.pool.empty()) {
+    hipEvent_t e = t.pool.back();
+    t.pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Folds finished launches into the totals; waits for them if `wait`.
+hipError_t drain(Timing &t, bool wait) {
+  hipError_t err = hipSuccess;
+  std::vector<TimedLaunch> keep;
+  for (auto &l : t.pending) {
+    hipError_t q = wait ? hipEventSynchronize(l.stop) : hipEventQuery(l.stop);
+    if (q == hipErrorNotReady) {
+      keep.push_back(l);
+      continue;
+    }
+    float ms = 0.f;
+    if (q == hipSuccess) q = hipEventElapsedTime(&ms, l.start, l.stop);
+    if (q != hipSuccess && err == hipSuccess) err = q;
+    t.launches[l.id] += 1;
+    t.total_ms[l.id] += ms;
+    t.pool.push_back(l.start);
+    t.pool.push_back(l.stop);
+  }
+  t.pending.swap(keep);
+  return err;
+}
+
+// Runs `launch` on stream s, bracketed by events when timing is enabled.
+template <typename F>
+hipError_t timed(int id, hipStream_t s, F &&launch) {
+  Timing &t = timing();
+  std::unique_lock<std::mutex> lock(t.mu);
+  if (!t.enabled) {
+    lock.unlock();
+    return launch();
+  }
+  hipEvent_t a = take_event(t), b = take_event(t);
+  if (!a || !b) return hipErrorOutOfMemory;
+  hipError_t e = hipEventRecord(a, s);
+  if (e == hipSuccess) e = launch();
+  if (e == hipSuccess) e = hipEventRecord(b, s);
+  if (e != hipSuccess) {
+    t.pool.push_back(a);
+    t.pool.push_back(b);
+    return e;
+  }
+  t.pending.push_back({id, a, b});
+  if (t.pending.size() > 4096) drain(t, false);
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t pg_pack_buffer_size(const pg_groups *g) {
+  int64_t T, n_resp, n_qt, n_kvt;
+  if (check_groups(g, &T, &n_resp, &n_qt, &n_kvt) != PG_OK) return 0;
+  return make_layout(T, g->num_groups, n_resp, n_qt, n_kvt).total;
+}
+
+pg_status pg_pack_host(const pg_groups *g, void *h_buf, size_t buf_bytes, int32_t *h_pos_ids,
+                       pg_desc *out) {
+  if (!h_buf || !out) return fail(PG_ERR_INVALID_ARG, "h_buf and out must not be NULL");
+  Layout L;
+  pg_desc d;
+  pg_status st = build_plan(g, static_cast<char *>(h_buf), buf_bytes, h_pos_ids, &d, &L);
+  if (st != PG_OK) return st;
+  point_into(&d, L, static_cast<const char *>(h_buf));
+  *out = d;
+  return PG_OK;
+}
+
+pg_status pg_pack(const pg_groups *g, void *d_buf, size_t buf_bytes, int32_t *d_pos_ids,
+                  pg_desc *out, void *stream) {
+  if (!d_buf || !out) return fail(PG_ERR_INVALID_ARG, "d_buf and out must not be NULL");
+  if (!aligned16(d_buf)) return fail(PG_ERR_INVALID_ARG, "d_buf is not 16-byte aligned");
+  int64_t T, n_resp, n_qt, n_kvt;
+  pg_status st = check_groups(g, &T, &n_resp, &n_qt, &n_kvt);
+  if (st != PG_OK) return st;
+  Layout L0 = make_layout(T, g->num_groups, n_resp, n_qt, n_kvt);
+  if (buf_bytes < L0.total)
+    return fail(PG_ERR_WORKSPACE, "descriptor buffer too small: need " + std::to_string(L0.total) +
+                                      " bytes, got " + std::to_string(buf_bytes));
+  std::vector<char> host(L0.total);
+  std::vector<int32_t> pos(d_pos_ids ? size_t(T) : 0);
+  Layout L;
+  pg_desc d;
+  st = build_plan(g, host.data(), host.size(), d_pos_ids ? pos.data() : nullptr, &d, &L);
+  if (st != PG_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(d_buf, host.data(), L.total, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess && d_pos_ids && T > 0)
+    e = hipMemcpyAsync(d_pos_ids, pos.data(), size_t(T) * 4, hipMemcpyHostToDevice, s);
+  // the host staging vectors die with this call, so wait for the copies
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_status(e, "pg_pack copy");
+  point_into(&d, L, static_cast<const char *>(d_buf));
+  *out = d;
+  return PG_OK;
+}
+
+pg_status pg_attn_fwd(const pg_desc *d, pg_dtype t, float softmax_scale, const void *q,
+                      const void *k, const void *v, void *o, float *lse, void *stream) {
+  pg_status st = check_desc(d);
+  if (st != PG_OK) return st;
+  if ((st = check_dtype(t)) != PG_OK) return st;
+  if (d->total_rows == 0) return PG_OK;
+  if ((st = check_ptrs({{q, "q"}, {k, "k"}, {v, "v"}, {o, "o"}, {lse, "lse"}})) != PG_OK) return st;
+  pg::Plan p = plan_of(d);
+  const float scale = resolve_scale(softmax_scale, p.D);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = timed(PG_KERNEL_FWD, s, [&] {
+    return (t == PG_BF16) ? pg::launch_fwd_bf16(p, scale, q, k, v, o, lse, s)
+                          : pg::launch_fwd_f32(p, scale, q, k, v, o, lse, s);
+  });
+  return hip_status(e, "pg_attn_fwd launch");
+}
+
+size_t pg_attn_bwd_workspace_size(const pg_desc *d, pg_dtype t) {
+  (void)t;
+  if (check_desc(d) != PG_OK) return 0;
+  return std::max<size_t>(16, align16(size_t(d->num_q_heads) * size_t(d->total_rows) * 4));
+}
+
+pg_status pg_attn_bwd(const pg_desc *d, pg_dtype t, float softmax_scale, const void *q,
+                      const void *k, const void *v, const void *o, const float *lse,
+                      const void *dout, void *dq, void *dk, void *dv, void *workspace,
+                      size_t ws_bytes, void *stream) {
+  pg_status st = check_desc(d);
+  if (st != PG_OK) return st;
+  if ((st = check_dtype(t)) != PG_OK) return st;
+  if (d->total_rows == 0) return PG_OK;
+  if ((st = check_ptrs({{q, "q"}, {k, "k"}, {v, "v"}, {o, "o"}, {lse, "lse"}, {dout, "dout"},
+                        {dq, "dq"}, {dk, "dk"}, {dv, "dv"}, {workspace, "workspace"}})) != PG_OK)
+    return st;
+  const size_t need = pg_attn_bwd_workspace_size(d, t);
+  if (ws_bytes < need)
+    return fail(PG_ERR_WORKSPACE, "workspace too small: need " + std::to_string(need) +
+                                      " bytes, got " + std::to_string(ws_bytes));
+  pg::Plan p = plan_of(d);
+  const float scale = resolve_scale(softmax_scale, p.D);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float *delta = static_cast<float *>(workspace);
+  hipError_t e = timed(PG_KERNEL_BWD_PRE, s, [&] { return pg::launch_bwd_pre(p, t, o, dout, delta, s); });
+  if (e != hipSuccess) return hip_status(e, "pg_attn_bwd preprocess launch");
+  e = timed(PG_KERNEL_BWD_DKDV, s, [&] {
+    return (t == PG_BF16) ? pg::launch_bwd_dkdv_bf16(p, scale, q, k, v, lse, delta, dout, dk, dv, s)
+                          : pg::launch_bwd_dkdv_f32(p, scale, q, k, v, lse, delta, dout, dk, dv, s);
+  });
+  if (e == hipSuccess)
+    e = timed(PG_KERNEL_BWD_DQ, s, [&] {
+      return (t == PG_BF16) ? pg::launch_bwd_dq_bf16(p, scale, q, k, v, lse, delta, dout, dq, s)
+                            : pg::launch_bwd_dq_f32(p, scale, q, k, v, lse, delta, dout, dq, s);
+    });
+  return hip_status(e, "pg_attn_bwd launch");
+}
+
+pg_status pg_rope(const pg_desc *d, pg_dtype t, void *x, int32_t num_heads, int32_t head_dim,
+                  const int32_t *pos_ids, float theta, int32_t inverse, void *stream) {
+  pg_status st = check_desc(d);
+  if (st != PG_OK) return st;
+  if ((st = check_dtype(t)) != PG_OK) return st;
+  if (num_heads <= 0 || head_dim <= 0 || (head_dim & 1))
+    return fail(PG_ERR_INVALID_ARG, "num_heads must be > 0 and head_dim even and > 0");
+  if (!(theta > 1.0f)) return fail(PG_ERR_INVALID_ARG, "theta must be > 1");
+  if (d->total_rows == 0) return PG_OK;
+  if ((st = check_ptrs({{x, "x"}, {pos_ids, "pos_ids"}})) != PG_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return hip_status(timed(PG_KERNEL_ROPE, s, [&] {
+                      return pg::launch_rope(d->total_rows, num_heads, head_dim, t, x, pos_ids,
+                                             theta, inverse, s);
+                    }),
+                    "pg_rope launch");
+}
+
+pg_status pg_kernel_timing(int32_t enable) {
+  Timing &t = timing();
+  std::lock_guard<std::mutex> lock(t.mu);
+  hipError_t e = drain(t, true);
+  for (int i = 0; i < PG_KERNEL_COUNT; ++i) {
+    t.launches[i] = 0;
+    t.total_ms[i] = 0.0;
+  }
+  t.enabled = enable != 0;
+  return hip_status(e, "pg_kernel_timing");
+}
+
+pg_status pg_kernel_times(int32_t kernel_id, int64_t *launches, double *total_ms) {
+  if (kernel_id < 0 || kernel_id >= PG_KERNEL_COUNT || !launches || !total_ms)
+    return fail(PG_ERR_INVALID_ARG, "unknown kernel id or NULL output");
+  Timing &t = timing();
+  std::lock_guard<std::mutex> lock(t.mu);
+  hipError_t e = drain(t, true);
+  *launches = t.launches[kernel_id];
+  *total_ms = t.total_ms[kernel_id];
+  return hip_status(e, "pg_kernel_times");
+}
+
+const char *pg_kernel_name(int32_t kernel_id) {
+  return (kernel_id >= 0 && kernel_id < PG_KERNEL_COUNT) ? kKernelNames[kernel_id] : nullptr;
+}
+
+const char *pg_last_error(void) { return g_last_error.c_str(); }
+
+const char *pg_version(void) { return "pg_attn 0.1 (gfx950)"; }
+
+}  // extern "C"

@@ -1,0 +1,520 @@
+// Grouped shared-prefix attention, backward, bf16 storage / fp32 accumulation,
+// for gfx950 (CDNA4, wave64, v_mfma_f32_32x32x16_bf16).
+//
+// The softmax is recomputed from the logsumexp saved by the forward pass.
+// Gradients equal those of the repeated-prefix baseline (Pith review of
+// Prefix Grouper, "Core claim", Lemma 2.1): the dK/dV of a prefix key row is
+// the sum over every query row that sees it -- the later prefix rows and every
+// row of all G responses of the group -- which in the baseline is the sum over
+// the G prefix copies.  No floating-point atomics are used:
+//   * dkdv: key-stationary.  A workgroup owns 128 key rows of one key/value
+//     head and walks, in a fixed order, every query head of that kv head and
+//     every 64-row query chunk in [k0, q_end), accumulating dK^T and dV^T in
+//     registers.  For a prefix tile that walk covers the prefix rows and all
+//     responses of the group, so the group reduction of Lemma 2.1 happens in
+//     registers, in a fixed order.
+//   * dq: query-stationary, over the same two key segments as the forward.
+// Both are deterministic: every output element is written by exactly one
+// lane, after a reduction whose order does not depend on scheduling.
+
+#include "pg_device.h"
+#include "pg_internal.h"
+
+namespace pg {
+namespace {
+
+// ---------------------------------------------------------------- preprocess
+// delta[h][t] = sum_d dO[t][h][d] * O[t][h][d], in float.
+template <typename Tin, int D>
+__global__ __launch_bounds__(256) void bwd_pre_kernel(const Tin *__restrict__ O,
+                                                      const Tin *__restrict__ dO,
+                                                      float *__restrict__ delta, int T, int Hq) {
+  constexpr int TPR = D / 8;            // threads per (row, head), 8 elements each
+  constexpr int RPB = 256 / TPR;        // (row, head) pairs per block
+  const int tid = threadIdx.x;
+  const long long rh = (long long)blockIdx.x * RPB + tid / TPR;
+  const int part = tid % TPR;
+  float acc = 0.f;
+  if (rh < (long long)T * Hq) {
+    const Tin *o = O + rh * D + part * 8;
+    const Tin *g = dO + rh * D + part * 8;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc += (float)o[j] * (float)g[j];
+  }
+#pragma unroll
+  for (int w = TPR / 2; w >= 1; w >>= 1) acc += __shfl_xor(acc, w);
+  if (rh < (long long)T * Hq && part == 0) {
+    const int t = (int)(rh / Hq), h = (int)(rh % Hq);
+    delta[(size_t)h * T + t] = acc;
+  }
+}
+
+// ---------------------------------------------------------------- dK, dV
+template <int D>
+struct DkdvCfg {
+  static constexpr int BN = PG_TILE_KV;  // key rows per workgroup
+  static constexpr int NW = BN / 32;     // waves (32 key rows each)
+  static constexpr int NT = NW * 64;
+  static constexpr int BM = 32;          // query rows per chunk
+  static constexpr int QS = D + 8;       // LDS stride of row-major Q, dO
+  static constexpr int TS = BM + 8;      // LDS stride of transposed Q^T, dO^T
+  static constexpr int C8 = D / 8;
+  static constexpr int LOADS = (BM * C8 + NT - 1) / NT;
+  static constexpr int NQB = BM / 32;    // 32-row query blocks per chunk
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void dkdv_bf16_kernel(
+    const int32_t *__restrict__ kv_tiles, const int32_t *__restrict__ row_hi,
+    const bf16 *__restrict__ Q, const bf16 *__restrict__ K, const bf16 *__restrict__ V,
+    const float *__restrict__ LSE, const float *__restrict__ Delta, const bf16 *__restrict__ dO,
+    bf16 *__restrict__ dK, bf16 *__restrict__ dV, int T, int Hq, int Hkv, float scale_log2,
+    float scale) {
+  using C = DkdvCfg<D>;
+  __shared__ __attribute__((aligned(16))) bf16 sQ[C::BM * C::QS];
+  __shared__ __attribute__((aligned(16))) bf16 sQt[D * C::TS];
+  __shared__ __attribute__((aligned(16))) bf16 sdO[C::BM * C::QS];
+  __shared__ __attribute__((aligned(16))) bf16 sdOt[D * C::TS];
+  __shared__ __attribute__((aligned(16))) float sL[C::BM];
+  __shared__ __attribute__((aligned(16))) float sDl[C::BM];
+
+  const int tile = blockIdx.x / Hkv;
+  const int hk = blockIdx.x - tile * Hkv;
+  const int rep = Hq / Hkv;
+  const int k0 = kv_tiles[4 * tile + 0], k1 = kv_tiles[4 * tile + 1];
+  const int qend = kv_tiles[4 * tile + 2];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+
+  const int kw0 = k0 + wave * 32;
+  const int kwl = min(k1, kw0 + 32) - 1;
+  const bool wave_active = kw0 < k1;
+  const int key = kw0 + l32;
+  const bool key_ok = key < k1;
+  const int hik = key_ok ? row_hi[key] : 0;  // queries [key, hik) see this key
+  // smallest / largest visibility end over the wave's keys
+  int min_hi = key_ok ? hik : 0x7fffffff, max_hi = hik;
+#pragma unroll
+  for (int w = 32; w >= 1; w >>= 1) {
+    min_hi = min(min_hi, __shfl_xor(min_hi, w));
+    max_hi = max(max_hi, __shfl_xor(max_hi, w));
+  }
+
+  // K and V rows of this wave as MFMA B operands: column = key l32, k = d.
+  bf16x8 kf[D / 16], vf[D / 16];
+  {
+    const size_t base = ((size_t)key * Hkv + hk) * D + 8 * hi;
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) {
+      if (key_ok) {
+        kf[st] = *reinterpret_cast<const bf16x8 *>(K + base + 16 * st);
+        vf[st] = *reinterpret_cast<const bf16x8 *>(V + base + 16 * st);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          kf[st][j] = (__bf16)0.f;
+          vf[st][j] = (__bf16)0.f;
+        }
+      }
+    }
+  }
+
+  f32x16 dk[D / 32], dv[D / 32];
+#pragma unroll
+  for (int nb = 0; nb < D / 32; ++nb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      dk[nb][r] = 0.f;
+      dv[nb][r] = 0.f;
+    }
+
+  const int nQ = (qend - k0 + C::BM - 1) / C::BM;  // chunks per query head
+  const int nC = nQ * rep;
+  const size_t q_row = (size_t)Hq * D;
+  u32x4 qreg[C::LOADS], oreg[C::LOADS];
+  float lreg = 0.f;
+  auto chunk_of = [&](int ci, int &h, int &c0) {
+    const int hh = ci / nQ;
+    h = hk * rep + hh;
+    c0 = k0 + (ci - hh * nQ) * C::BM;
+  };
+  auto load_chunk = [&](int h, int c0) {
+#pragma unroll
+    for (int i = 0; i < C::LOADS; ++i) {
+      const int idx = i * C::NT + tid;
+      const int row = idx / C::C8, c8 = idx % C::C8;
+      const int qr = c0 + row;
+      if (idx < C::BM * C::C8 && qr < T) {
+        const size_t off = (size_t)qr * q_row + (size_t)h * D + c8 * 8;
+        qreg[i] = *reinterpret_cast<const u32x4 *>(Q + off);
+        oreg[i] = *reinterpret_cast<const u32x4 *>(dO + off);
+      } else {
+        qreg[i] = u32x4{0, 0, 0, 0};
+        oreg[i] = u32x4{0, 0, 0, 0};
+      }
+    }
+    if (tid < 2 * C::BM) {
+      const int row = tid % C::BM;
+      const int qr = c0 + row;
+      if (qr < T)
+        lreg = tid < C::BM ? LSE[(size_t)h * T + qr] * kLog2e : Delta[(size_t)h * T + qr];
+      else
+        lreg = 0.f;
+    }
+  };
+  auto store_chunk = [&]() {
+#pragma unroll
+    for (int i = 0; i < C::LOADS; ++i) {
+      const int idx = i * C::NT + tid;
+      if (idx < C::BM * C::C8) {
+        const int row = idx / C::C8, c8 = idx % C::C8;
+        *reinterpret_cast<u32x4 *>(&sQ[row * C::QS + c8 * 8]) = qreg[i];
+        *reinterpret_cast<u32x4 *>(&sdO[row * C::QS + c8 * 8]) = oreg[i];
+        const bf16x8 qv = __builtin_bit_cast(bf16x8, qreg[i]);
+        const bf16x8 ov = __builtin_bit_cast(bf16x8, oreg[i]);
+        const int col = swap23(row);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          sQt[(c8 * 8 + j) * C::TS + col] = qv[j];
+          sdOt[(c8 * 8 + j) * C::TS + col] = ov[j];
+        }
+      }
+    }
+    if (tid < C::BM)
+      sL[tid] = lreg;
+    else if (tid < 2 * C::BM)
+      sDl[tid - C::BM] = lreg;
+  };
+
+  if (nC > 0) {
+    int h, c0;
+    chunk_of(0, h, c0);
+    load_chunk(h, c0);
+  }
+  for (int ci = 0; ci < nC; ++ci) {
+    int h, c0;
+    chunk_of(ci, h, c0);
+    __syncthreads();
+    store_chunk();
+    __syncthreads();
+    if (ci + 1 < nC) {
+      int h2, c2;
+      chunk_of(ci + 1, h2, c2);
+      load_chunk(h2, c2);
+    }
+    if (!wave_active) continue;
+    if (c0 + C::BM - 1 < kw0) continue;  // every query precedes every key
+    if (c0 >= max_hi) continue;          // no key of this wave is seen this far
+    const bool full = (c0 >= kwl) && (c0 + C::BM <= min_hi);
+
+#pragma unroll
+    for (int qb = 0; qb < C::NQB; ++qb) {
+      f32x16 s, dp;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s[r] = 0.f;
+        dp[r] = 0.f;
+      }
+#pragma unroll
+      for (int st = 0; st < D / 16; ++st) {
+        const int off = (qb * 32 + l32) * C::QS + st * 16 + hi * 8;
+        s = mfma32(*reinterpret_cast<const bf16x8 *>(&sQ[off]), kf[st], s);
+        dp = mfma32(*reinterpret_cast<const bf16x8 *>(&sdO[off]), vf[st], dp);
+      }
+      // register r holds query c0 + qb*32 + mfma_row(r, hi); lane column is the key
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const int ql = qb * 32 + rq * 8 + hi * 4;
+        const f32x4 Lq = *reinterpret_cast<const f32x4 *>(&sL[ql]);
+        const f32x4 Dq = *reinterpret_cast<const f32x4 *>(&sDl[ql]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = rq * 4 + j;
+          float p = fast_exp2(s[r] * scale_log2 - Lq[j]);
+          if (!full) {
+            const int qr = c0 + ql + j;
+            p = (key <= qr && qr < hik) ? p : 0.f;
+          }
+          s[r] = p;
+          dp[r] = p * (dp[r] - Dq[j]);
+        }
+      }
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        const bf16x8 pb = pack8(s, sub * 8);
+        const bf16x8 db = pack8(dp, sub * 8);
+#pragma unroll
+        for (int nb = 0; nb < D / 32; ++nb) {
+          const int off = (nb * 32 + l32) * C::TS + qb * 32 + sub * 16 + hi * 8;
+          dv[nb] = mfma32(*reinterpret_cast<const bf16x8 *>(&sdOt[off]), pb, dv[nb]);
+          dk[nb] = mfma32(*reinterpret_cast<const bf16x8 *>(&sQt[off]), db, dk[nb]);
+        }
+      }
+    }
+  }
+
+  if (!wave_active || !key_ok) return;
+  bf16 *dkp = dK + ((size_t)key * Hkv + hk) * D;
+  bf16 *dvp = dV + ((size_t)key * Hkv + hk) * D;
+#pragma unroll
+  for (int nb = 0; nb < D / 32; ++nb)
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq) {
+      const int d0 = nb * 32 + rq * 8 + hi * 4;
+      *reinterpret_cast<u32x2 *>(dkp + d0) =
+          pack4_bf16(dk[nb][rq * 4 + 0] * scale, dk[nb][rq * 4 + 1] * scale,
+                     dk[nb][rq * 4 + 2] * scale, dk[nb][rq * 4 + 3] * scale);
+      *reinterpret_cast<u32x2 *>(dvp + d0) =
+          pack4_bf16(dv[nb][rq * 4 + 0], dv[nb][rq * 4 + 1], dv[nb][rq * 4 + 2], dv[nb][rq * 4 + 3]);
+    }
+}
+
+// ---------------------------------------------------------------- dQ
+template <int D>
+struct DqCfg {
+  static constexpr int BM = PG_TILE_Q;  // query rows per workgroup
+  static constexpr int NW = BM / 32;
+  static constexpr int NT = NW * 64;
+  static constexpr int BN = 64;         // keys per chunk
+  static constexpr int KS = D + 8;
+  static constexpr int TS = BN + 8;
+  static constexpr int C8 = D / 8;
+  static constexpr int LOADS = BN * C8 / NT;
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void dq_bf16_kernel(
+    const int32_t *__restrict__ q_tiles, const int32_t *__restrict__ row_lo,
+    const bf16 *__restrict__ Q, const bf16 *__restrict__ K, const bf16 *__restrict__ V,
+    const float *__restrict__ LSE, const float *__restrict__ Delta, const bf16 *__restrict__ dO,
+    bf16 *__restrict__ dQ, int T, int Hq, int Hkv, float scale_log2, float scale) {
+  using C = DqCfg<D>;
+  __shared__ __attribute__((aligned(16))) bf16 sK[C::BN * C::KS];
+  __shared__ __attribute__((aligned(16))) bf16 sKt[D * C::TS];
+  __shared__ __attribute__((aligned(16))) bf16 sV[C::BN * C::KS];
+
+  const int tile = blockIdx.x / Hq;
+  const int h = blockIdx.x - tile * Hq;
+  const int hk = h / (Hq / Hkv);
+  const int q0 = q_tiles[4 * tile + 0], q1 = q_tiles[4 * tile + 1];
+  const int g0 = q_tiles[4 * tile + 2], pe = q_tiles[4 * tile + 3];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+
+  const int qw0 = q0 + wave * 32;
+  const int qwl = min(q1, qw0 + 32) - 1;
+  const bool wave_active = qw0 < q1;
+  const int qrow = qw0 + l32;
+  const bool row_ok = qrow < q1;
+  const int lo = row_ok ? row_lo[qrow] : 0;
+  const int lo_first = wave_active ? row_lo[qw0] : 0;
+  const int lo_last = wave_active ? row_lo[qwl] : 0;
+  const float Lq = row_ok ? LSE[(size_t)h * T + qrow] * kLog2e : 0.f;
+  const float Dq = row_ok ? Delta[(size_t)h * T + qrow] : 0.f;
+
+  bf16x8 qf[D / 16], of[D / 16];
+  {
+    const size_t base = ((size_t)qrow * Hq + h) * D + 8 * hi;
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) {
+      if (row_ok) {
+        qf[st] = *reinterpret_cast<const bf16x8 *>(Q + base + 16 * st);
+        of[st] = *reinterpret_cast<const bf16x8 *>(dO + base + 16 * st);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          qf[st][j] = (__bf16)0.f;
+          of[st][j] = (__bf16)0.f;
+        }
+      }
+    }
+  }
+
+  const int a0 = g0, a1 = min(pe, q1);
+  const int b0 = max(pe, row_lo[q0]), b1 = q1;
+  const int nA = a1 > a0 ? (a1 - a0 + C::BN - 1) / C::BN : 0;
+  const int nB = b1 > b0 ? (b1 - b0 + C::BN - 1) / C::BN : 0;
+  const int nC = nA + nB;
+
+  const size_t kv_row = (size_t)Hkv * D;
+  const bf16 *Kh = K + (size_t)hk * D;
+  const bf16 *Vh = V + (size_t)hk * D;
+  u32x4 kreg[C::LOADS], vreg[C::LOADS];
+  auto load_chunk = [&](int c0) {
+#pragma unroll
+    for (int i = 0; i < C::LOADS; ++i) {
+      const int idx = i * C::NT + tid;
+      const int row = idx / C::C8, c8 = idx % C::C8;
+      const int kr = c0 + row;
+      if (kr < T) {
+        kreg[i] = *reinterpret_cast<const u32x4 *>(Kh + kr * kv_row + c8 * 8);
+        vreg[i] = *reinterpret_cast<const u32x4 *>(Vh + kr * kv_row + c8 * 8);
+      } else {
+        kreg[i] = u32x4{0, 0, 0, 0};
+        vreg[i] = u32x4{0, 0, 0, 0};
+      }
+    }
+  };
+  auto store_chunk = [&]() {
+#pragma unroll
+    for (int i = 0; i < C::LOADS; ++i) {
+      const int idx = i * C::NT + tid;
+      const int row = idx / C::C8, c8 = idx % C::C8;
+      *reinterpret_cast<u32x4 *>(&sK[row * C::KS + c8 * 8]) = kreg[i];
+      *reinterpret_cast<u32x4 *>(&sV[row * C::KS + c8 * 8]) = vreg[i];
+      const bf16x8 kv = __builtin_bit_cast(bf16x8, kreg[i]);
+      const int col = swap23(row);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) sKt[(c8 * 8 + j) * C::TS + col] = kv[j];
+    }
+  };
+  auto chunk_range = [&](int ci, int &c0, int &cend) {
+    if (ci < nA) {
+      c0 = a0 + ci * C::BN;
+      cend = a1;
+    } else {
+      c0 = b0 + (ci - nA) * C::BN;
+      cend = b1;
+    }
+  };
+
+  f32x16 dq[D / 32];
+#pragma unroll
+  for (int nb = 0; nb < D / 32; ++nb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dq[nb][r] = 0.f;
+
+  if (nC > 0) {
+    int c0, cend;
+    chunk_range(0, c0, cend);
+    load_chunk(c0);
+  }
+  for (int ci = 0; ci < nC; ++ci) {
+    int c0, cend;
+    chunk_range(ci, c0, cend);
+    __syncthreads();
+    store_chunk();
+    __syncthreads();
+    if (ci + 1 < nC) {
+      int n0, nend;
+      chunk_range(ci + 1, n0, nend);
+      load_chunk(n0);
+    }
+    if (!wave_active) continue;
+    const int clast = min(c0 + C::BN, cend) - 1;
+    if (c0 > qwl) continue;
+    if (c0 >= pe && clast < lo_first) continue;
+    const bool full = (c0 + C::BN <= cend) && (c0 + C::BN - 1 <= qw0) &&
+                      (c0 + C::BN <= pe || c0 >= lo_last);
+
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      f32x16 s, dp;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s[r] = 0.f;
+        dp[r] = 0.f;
+      }
+#pragma unroll
+      for (int st = 0; st < D / 16; ++st) {
+        const int off = (b * 32 + l32) * C::KS + st * 16 + hi * 8;
+        s = mfma32(*reinterpret_cast<const bf16x8 *>(&sK[off]), qf[st], s);
+        dp = mfma32(*reinterpret_cast<const bf16x8 *>(&sV[off]), of[st], dp);
+      }
+      // register r holds key c0 + b*32 + mfma_row(r, hi); lane column is the query
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p = fast_exp2(s[r] * scale_log2 - Lq);
+        if (!full) {
+          const int kr = c0 + b * 32 + mfma_row(r, hi);
+          const bool ok = kr < cend && kr <= qrow && (kr < pe || kr >= lo);
+          p = ok ? p : 0.f;
+        }
+        s[r] = p * (dp[r] - Dq);
+      }
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        const bf16x8 db = pack8(s, sub * 8);
+#pragma unroll
+        for (int nb = 0; nb < D / 32; ++nb) {
+          const int off = (nb * 32 + l32) * C::TS + b * 32 + sub * 16 + hi * 8;
+          dq[nb] = mfma32(*reinterpret_cast<const bf16x8 *>(&sKt[off]), db, dq[nb]);
+        }
+      }
+    }
+  }
+
+  if (!wave_active || !row_ok) return;
+  bf16 *qp = dQ + ((size_t)qrow * Hq + h) * D;
+#pragma unroll
+  for (int nb = 0; nb < D / 32; ++nb)
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq) {
+      const int d0 = nb * 32 + rq * 8 + hi * 4;
+      *reinterpret_cast<u32x2 *>(qp + d0) =
+          pack4_bf16(dq[nb][rq * 4 + 0] * scale, dq[nb][rq * 4 + 1] * scale,
+                     dq[nb][rq * 4 + 2] * scale, dq[nb][rq * 4 + 3] * scale);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_bwd_pre(const Plan &p, pg_dtype t, const void *o, const void *dout,
+                          float *delta, hipStream_t s) {
+  const long long rows = (long long)p.T * p.Hq;
+  if (rows == 0) return hipSuccess;
+  const int rpb = 256 / (p.D / 8);
+  const dim3 grid((unsigned)((rows + rpb - 1) / rpb)), block(256);
+  if (t == PG_BF16) {
+    if (p.D == 128)
+      hipLaunchKernelGGL((bwd_pre_kernel<__bf16, 128>), grid, block, 0, s, (const __bf16 *)o,
+                         (const __bf16 *)dout, delta, p.T, p.Hq);
+    else
+      hipLaunchKernelGGL((bwd_pre_kernel<__bf16, 64>), grid, block, 0, s, (const __bf16 *)o,
+                         (const __bf16 *)dout, delta, p.T, p.Hq);
+  } else {
+    if (p.D == 128)
+      hipLaunchKernelGGL((bwd_pre_kernel<float, 128>), grid, block, 0, s, (const float *)o,
+                         (const float *)dout, delta, p.T, p.Hq);
+    else
+      hipLaunchKernelGGL((bwd_pre_kernel<float, 64>), grid, block, 0, s, (const float *)o,
+                         (const float *)dout, delta, p.T, p.Hq);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dkdv_bf16(const Plan &p, float scale, const void *q, const void *k,
+                                const void *v, const float *lse, const float *delta,
+                                const void *dout, void *dk, void *dv, hipStream_t s) {
+  if (p.n_kv_tiles == 0) return hipSuccess;
+  const dim3 grid((unsigned)p.n_kv_tiles * (unsigned)p.Hkv), block(256);
+  const float sl2 = scale * kLog2e;
+  if (p.D == 128)
+    hipLaunchKernelGGL(dkdv_bf16_kernel<128>, grid, block, 0, s, p.kv_tiles, p.row_hi,
+                       (const bf16 *)q, (const bf16 *)k, (const bf16 *)v, lse, delta,
+                       (const bf16 *)dout, (bf16 *)dk, (bf16 *)dv, p.T, p.Hq, p.Hkv, sl2, scale);
+  else
+    hipLaunchKernelGGL(dkdv_bf16_kernel<64>, grid, block, 0, s, p.kv_tiles, p.row_hi,
+                       (const bf16 *)q, (const bf16 *)k, (const bf16 *)v, lse, delta,
+                       (const bf16 *)dout, (bf16 *)dk, (bf16 *)dv, p.T, p.Hq, p.Hkv, sl2, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dq_bf16(const Plan &p, float scale, const void *q, const void *k,
+                              const void *v, const float *lse, const float *delta,
+                              const void *dout, void *dq, hipStream_t s) {
+  if (p.n_q_tiles == 0) return hipSuccess;
+  const dim3 grid((unsigned)p.n_q_tiles * (unsigned)p.Hq), block(256);
+  const float sl2 = scale * kLog2e;
+  if (p.D == 128)
+    hipLaunchKernelGGL(dq_bf16_kernel<128>, grid, block, 0, s, p.q_tiles, p.row_lo,
+                       (const bf16 *)q, (const bf16 *)k, (const bf16 *)v, lse, delta,
+                       (const bf16 *)dout, (bf16 *)dq, p.T, p.Hq, p.Hkv, sl2, scale);
+  else
+    hipLaunchKernelGGL(dq_bf16_kernel<64>, grid, block, 0, s, p.q_tiles, p.row_lo,
+                       (const bf16 *)q, (const bf16 *)k, (const bf16 *)v, lse, delta,
+                       (const bf16 *)dout, (bf16 *)dq, p.T, p.Hq, p.Hkv, sl2, scale);
+  return hipGetLastError();
+}
+
+}  // namespace pg

@@ -1,0 +1,74 @@
+// Device helpers for the gfx950 (CDNA4) kernels of libpg_attn.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pg {
+
+typedef __bf16 bf16;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+
+// Score value of a masked (query, key) pair, in the base-2 domain.  Finite, so
+// that a row whose first chunk is entirely masked produces exp2(0) garbage
+// instead of NaN; the garbage is wiped by the exp2(m_old - m_new) = 0 rescale
+// when the row meets its first visible key (every row sees at least itself).
+constexpr float kMasked = -1.0e30f;
+
+// D(32x32, f32) += A(32x16, bf16) * B(16x32, bf16).
+// Operand lanes: A row m = lane % 32, B column n = lane % 32; the 8 k values a
+// lane supplies are indexed by (lane / 32, slot) identically for A and B, so
+// any assignment of the contraction index to (lane / 32, slot) that both
+// operands share gives the same product.
+// Result: register r of lane l holds D[8 * (r / 4) + 4 * (l / 32) + r % 4][l % 32].
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Row of the 32x32 result held by register r in lane half `hi` (= lane / 32).
+__device__ __forceinline__ constexpr int mfma_row(int r, int hi) {
+  return 8 * (r >> 2) + 4 * hi + (r & 3);
+}
+
+// A transposed tile stored in LDS keeps, inside every 16-wide block of the
+// contraction index, position u at u with bits 2 and 3 swapped.  Then the 8
+// contraction values that lane half `hi` needs for one MFMA k-step (which are
+// mfma_row(sub * 8 + j, hi) for j = 0..7, i.e. offsets {0..3, 8..11} + 4 * hi)
+// sit contiguously at positions 8 * hi + j, and one 16-byte LDS read fetches
+// them.
+__device__ __forceinline__ constexpr int swap23(int u) {
+  return (u & ~12) | ((u & 4) << 1) | ((u & 8) >> 1);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float wave_swap_halves(float x) { return __shfl_xor(x, 32); }
+
+// Pack 8 floats (registers r0..r0+7 of a 32x32 result) into bf16x8.
+__device__ __forceinline__ bf16x8 pack8(const f32x16 &s, int r0) {
+  bf16x8 p;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) p[j] = (__bf16)s[r0 + j];
+  return p;
+}
+
+__device__ __forceinline__ u32x2 pack4_bf16(float a, float b, float c, float d) {
+  bf16x4 v;
+  v[0] = (__bf16)a;
+  v[1] = (__bf16)b;
+  v[2] = (__bf16)c;
+  v[3] = (__bf16)d;
+  return __builtin_bit_cast(u32x2, v);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t u) {
+  return __uint_as_float(uint32_t(u) << 16);
+}
+
+}  // namespace pg

@@ -1,0 +1,257 @@
+// Grouped shared-prefix attention, forward, bf16 storage / fp32 accumulation,
+// for gfx950 (CDNA4, wave64, v_mfma_f32_32x32x16_bf16).
+//
+// One launch covers both parts of the method's attention (Pith review of
+// Prefix Grouper, "What carries the argument"):
+//   * prefix rows: causal self-attention over the prefix only, once per group;
+//   * response rows: a two-segment pass over (A) every prefix key, with no
+//     mask, then (B) the keys of the row's own response up to itself.
+// A work item is up to 128 consecutive packed rows of one group and one query
+// head.  Rows of several responses may share a work item: segment A is the
+// same prefix K/V for all of them, so each prefix K/V chunk is staged through
+// LDS once and consumed by every response row of the item; segment B is masked
+// per row with the row's own response start (row_lo).  Both segments feed one
+// online softmax per row.
+//
+// Wave layout: 4 waves x 32 query rows.  Each wave computes S^T = K Q^T for a
+// 64-key chunk (A = K rows from LDS, B = the wave's Q rows held in registers),
+// so lane l owns query row l % 32 and its softmax statistics are per-lane
+// scalars; P^T then feeds O^T += V^T P^T directly from the accumulator
+// registers, with V stored transposed in LDS.
+
+#include "pg_device.h"
+#include "pg_internal.h"
+
+namespace pg {
+namespace {
+
+template <int D>
+struct FwdCfg {
+  static constexpr int BM = PG_TILE_Q;  // query rows per workgroup
+  static constexpr int NW = BM / 32;    // waves
+  static constexpr int NT = NW * 64;    // threads
+  static constexpr int BN = 64;         // keys per chunk
+  static constexpr int KS = D + 8;      // LDS row stride of K (elements)
+  static constexpr int VS = BN + 8;     // LDS row stride of V^T (elements)
+  static constexpr int C8 = D / 8;      // 16-byte pieces per row
+  static constexpr int LOADS = BN * C8 / NT;
+  static_assert(BN * C8 % NT == 0, "chunk must split evenly over the threads");
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void fwd_bf16_kernel(
+    const int32_t *__restrict__ q_tiles, const int32_t *__restrict__ row_lo,
+    const bf16 *__restrict__ Q, const bf16 *__restrict__ K, const bf16 *__restrict__ V,
+    bf16 *__restrict__ O, float *__restrict__ LSE, int T, int Hq, int Hkv, float scale_log2) {
+  using C = FwdCfg<D>;
+  __shared__ __attribute__((aligned(16))) bf16 sK[C::BN * C::KS];
+  __shared__ __attribute__((aligned(16))) bf16 sVt[D * C::VS];
+
+  const int tile = blockIdx.x / Hq;
+  const int h = blockIdx.x - tile * Hq;
+  const int hk = h / (Hq / Hkv);
+  const int q0 = q_tiles[4 * tile + 0], q1 = q_tiles[4 * tile + 1];
+  const int g0 = q_tiles[4 * tile + 2], pe = q_tiles[4 * tile + 3];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+
+  const int qw0 = q0 + wave * 32;         // first row of this wave
+  const int qwl = min(q1, qw0 + 32) - 1;  // last valid row of this wave
+  const bool wave_active = qw0 < q1;
+  const int qrow = qw0 + l32;
+  const bool row_ok = qrow < q1;
+  const int lo = row_ok ? row_lo[qrow] : 0;
+  const int lo_first = wave_active ? row_lo[qw0] : 0;
+  const int lo_last = wave_active ? row_lo[qwl] : 0;
+
+  // Q rows of this wave as MFMA B operands: column = query l32, k = 16 st + 8 hi + j.
+  bf16x8 qf[D / 16];
+  {
+    const bf16 *qp = Q + ((size_t)qrow * Hq + h) * D + 8 * hi;
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) {
+      if (row_ok) {
+        qf[st] = *reinterpret_cast<const bf16x8 *>(qp + 16 * st);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) qf[st][j] = (__bf16)0.f;
+      }
+    }
+  }
+
+  // Segment A: prefix keys [g0, min(pe, q1)).  Segment B: own-response keys
+  // [max(pe, row_lo[q0]), q1); row_lo is non-decreasing inside a group.
+  const int a0 = g0, a1 = min(pe, q1);
+  const int b0 = max(pe, row_lo[q0]), b1 = q1;
+  const int nA = a1 > a0 ? (a1 - a0 + C::BN - 1) / C::BN : 0;
+  const int nB = b1 > b0 ? (b1 - b0 + C::BN - 1) / C::BN : 0;
+  const int nC = nA + nB;
+
+  const size_t kv_row = (size_t)Hkv * D;
+  const bf16 *Kh = K + (size_t)hk * D;
+  const bf16 *Vh = V + (size_t)hk * D;
+  u32x4 kreg[C::LOADS], vreg[C::LOADS];
+  auto load_chunk = [&](int c0) {
+#pragma unroll
+    for (int i = 0; i < C::LOADS; ++i) {
+      const int idx = i * C::NT + tid;
+      const int row = idx / C::C8, c8 = idx % C::C8;
+      const int key = c0 + row;
+      if (key < T) {
+        kreg[i] = *reinterpret_cast<const u32x4 *>(Kh + key * kv_row + c8 * 8);
+        vreg[i] = *reinterpret_cast<const u32x4 *>(Vh + key * kv_row + c8 * 8);
+      } else {
+        kreg[i] = u32x4{0, 0, 0, 0};
+        vreg[i] = u32x4{0, 0, 0, 0};
+      }
+    }
+  };
+  auto store_chunk = [&]() {
+#pragma unroll
+    for (int i = 0; i < C::LOADS; ++i) {
+      const int idx = i * C::NT + tid;
+      const int row = idx / C::C8, c8 = idx % C::C8;
+      *reinterpret_cast<u32x4 *>(&sK[row * C::KS + c8 * 8]) = kreg[i];
+      const bf16x8 vv = __builtin_bit_cast(bf16x8, vreg[i]);
+      const int col = swap23(row);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) sVt[(c8 * 8 + j) * C::VS + col] = vv[j];
+    }
+  };
+  auto chunk_range = [&](int ci, int &c0, int &cend) {
+    if (ci < nA) {
+      c0 = a0 + ci * C::BN;
+      cend = a1;
+    } else {
+      c0 = b0 + (ci - nA) * C::BN;
+      cend = b1;
+    }
+  };
+
+  f32x16 o[D / 32];
+#pragma unroll
+  for (int nb = 0; nb < D / 32; ++nb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[nb][r] = 0.f;
+  float m = kMasked, l = 0.f;
+
+  if (nC > 0) {
+    int c0, cend;
+    chunk_range(0, c0, cend);
+    load_chunk(c0);
+  }
+  for (int ci = 0; ci < nC; ++ci) {
+    int c0, cend;
+    chunk_range(ci, c0, cend);
+    __syncthreads();  // LDS reads of the previous chunk are done
+    store_chunk();
+    __syncthreads();
+    if (ci + 1 < nC) {
+      int n0, nend;
+      chunk_range(ci + 1, n0, nend);
+      load_chunk(n0);  // in flight while this chunk is computed
+    }
+    if (!wave_active) continue;
+    const int clast = min(c0 + C::BN, cend) - 1;
+    if (c0 > qwl) continue;                       // every key follows every row
+    if (c0 >= pe && clast < lo_first) continue;   // keys of earlier responses only
+    const bool full = (c0 + C::BN <= cend) && (c0 + C::BN - 1 <= qw0) &&
+                      (c0 + C::BN <= pe || c0 >= lo_last);
+
+    f32x16 s[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[b][r] = 0.f;
+#pragma unroll
+      for (int st = 0; st < D / 16; ++st) {
+        const bf16x8 a =
+            *reinterpret_cast<const bf16x8 *>(&sK[(b * 32 + l32) * C::KS + st * 16 + hi * 8]);
+        s[b] = mfma32(a, qf[st], s[b]);
+      }
+    }
+    float mx = kMasked;
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float x = s[b][r] * scale_log2;
+        if (!full) {
+          const int key = c0 + b * 32 + mfma_row(r, hi);
+          const bool ok = key < cend && key <= qrow && (key < pe || key >= lo);
+          x = ok ? x : kMasked;
+        }
+        s[b][r] = x;
+        mx = fmaxf(mx, x);
+      }
+    mx = fmaxf(mx, wave_swap_halves(mx));
+    const float m_new = fmaxf(m, mx);
+    const float alpha = fast_exp2(m - m_new);
+    m = m_new;
+    float rs = 0.f;
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = fast_exp2(s[b][r] - m_new);
+        s[b][r] = p;
+        rs += p;
+      }
+    l = l * alpha + rs;
+#pragma unroll
+    for (int nb = 0; nb < D / 32; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[nb][r] *= alpha;
+    bf16x8 pf[2][2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) pf[b][sub] = pack8(s[b], sub * 8);
+#pragma unroll
+    for (int nb = 0; nb < D / 32; ++nb)
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8 *>(
+              &sVt[(nb * 32 + l32) * C::VS + b * 32 + sub * 16 + hi * 8]);
+          o[nb] = mfma32(a, pf[b][sub], o[nb]);
+        }
+  }
+
+  if (!wave_active) return;
+  const float lt = l + wave_swap_halves(l);
+  if (!row_ok) return;
+  const float inv = 1.f / lt;
+  bf16 *op = O + ((size_t)qrow * Hq + h) * D;
+#pragma unroll
+  for (int nb = 0; nb < D / 32; ++nb)
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq) {
+      const int d0 = nb * 32 + rq * 8 + hi * 4;
+      *reinterpret_cast<u32x2 *>(op + d0) =
+          pack4_bf16(o[nb][rq * 4 + 0] * inv, o[nb][rq * 4 + 1] * inv, o[nb][rq * 4 + 2] * inv,
+                     o[nb][rq * 4 + 3] * inv);
+    }
+  if (hi == 0) LSE[(size_t)h * T + qrow] = (m + __log2f(lt)) * kLn2;
+}
+
+}  // namespace
+
+hipError_t launch_fwd_bf16(const Plan &p, float scale, const void *q, const void *k,
+                           const void *v, void *o, float *lse, hipStream_t s) {
+  if (p.n_q_tiles == 0) return hipSuccess;
+  const dim3 grid((unsigned)p.n_q_tiles * (unsigned)p.Hq), block(256);
+  const float sl2 = scale * kLog2e;
+  if (p.D == 128)
+    hipLaunchKernelGGL(fwd_bf16_kernel<128>, grid, block, 0, s, p.q_tiles, p.row_lo,
+                       (const bf16 *)q, (const bf16 *)k, (const bf16 *)v, (bf16 *)o, lse, p.T,
+                       p.Hq, p.Hkv, sl2);
+  else
+    hipLaunchKernelGGL(fwd_bf16_kernel<64>, grid, block, 0, s, p.q_tiles, p.row_lo,
+                       (const bf16 *)q, (const bf16 *)k, (const bf16 *)v, (bf16 *)o, lse, p.T,
+                       p.Hq, p.Hkv, sl2);
+  return hipGetLastError();
+}
+
+}  // namespace pg

@@ -1,0 +1,52 @@
+// Internal declarations shared by the host API and the HIP kernel files of
+// libpg_attn.  Not part of the public C ABI (that is include/pg_attn.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pg_attn.h"
+
+namespace pg {
+
+// Everything a kernel launch needs from the descriptor, by value.
+struct Plan {
+  int T, Hq, Hkv, D;
+  int n_q_tiles, n_kv_tiles;
+  const int32_t *row_lo, *row_hi;
+  const int32_t *q_tiles, *kv_tiles;
+};
+
+// log2(e): scores are kept in the base-2 domain inside the kernels so that the
+// exponential is a single v_exp_f32.
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Forward (writes o and lse for every row and query head).
+hipError_t launch_fwd_bf16(const Plan &p, float scale, const void *q, const void *k,
+                           const void *v, void *o, float *lse, hipStream_t s);
+hipError_t launch_fwd_f32(const Plan &p, float scale, const void *q, const void *k,
+                          const void *v, void *o, float *lse, hipStream_t s);
+
+// Backward preprocess: delta[h][t] = sum_d dO[t][h][d] * O[t][h][d] (float).
+hipError_t launch_bwd_pre(const Plan &p, pg_dtype t, const void *o, const void *dout,
+                          float *delta, hipStream_t s);
+// dK, dV (key-stationary) and dQ (query-stationary); no atomics.
+hipError_t launch_bwd_dkdv_bf16(const Plan &p, float scale, const void *q, const void *k,
+                                const void *v, const float *lse, const float *delta,
+                                const void *dout, void *dk, void *dv, hipStream_t s);
+hipError_t launch_bwd_dq_bf16(const Plan &p, float scale, const void *q, const void *k,
+                              const void *v, const float *lse, const float *delta,
+                              const void *dout, void *dq, hipStream_t s);
+hipError_t launch_bwd_dkdv_f32(const Plan &p, float scale, const void *q, const void *k,
+                               const void *v, const float *lse, const float *delta,
+                               const void *dout, void *dk, void *dv, hipStream_t s);
+hipError_t launch_bwd_dq_f32(const Plan &p, float scale, const void *q, const void *k,
+                             const void *v, const float *lse, const float *delta,
+                             const void *dout, void *dq, hipStream_t s);
+
+// Rotary embedding in place.
+hipError_t launch_rope(int T, int H, int D, pg_dtype t, void *x, const int32_t *pos,
+                       float theta, int inverse, hipStream_t s);
+
+}  // namespace pg

@@ -1,0 +1,228 @@
+"""Host-side tests of libpg_attn: exports, planner, validation.  No GPU.
+
+The library is loaded and called only through entry points that touch no
+device: pg_pack_host (the planner into host memory), the size functions, and
+argument validation, which rejects the call before anything is enqueued.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import shared_prefix_grouped_amd as pg
+from oracle.attention import member_sequences, pair_counts, position_ids
+from tests.golden_io import read_visibility_fixture
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                      "pg_attn.h")
+
+
+def _lib():
+    try:
+        return pg.lib()
+    except pg.LibraryNotBuilt as e:  # the build step must have run first
+        pytest.fail(str(e))
+
+
+def test_exports_every_declared_function():
+    L = _lib()
+    text = open(HEADER).read()
+    names = set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]*?\b(pg_\w+)\s*\(", text, flags=re.M))
+    assert {"pg_pack", "pg_attn_fwd", "pg_attn_bwd", "pg_pack_host", "pg_rope"} <= names
+    for n in sorted(names):
+        assert hasattr(L, n), f"{n} declared in pg_attn.h but not exported"
+    assert set(pg.EXPORTED) == names
+
+
+def _visibility_from_plan(plan):
+    """Key k is visible to query q iff k <= q < row_hi[k]; check row_lo gives the same."""
+    T = plan["total_rows"]
+    hi = plan["row_hi"]
+    q = np.arange(T)[:, None]
+    k = np.arange(T)[None, :]
+    vis_hi = (k <= q) & (q < hi[None, :])
+    # row_lo form: k in [group start, prefix end) or [row_lo[q], q], within the group
+    gs, pe = plan["group_start"], plan["prefix_end"]
+    grp = np.searchsorted(gs, np.arange(T), side="right") - 1
+    g0 = gs[grp][:, None]
+    p_end = pe[grp][:, None]
+    vis_lo = (k >= g0) & (k <= q) & ((k < p_end) | (k >= plan["row_lo"][:, None]))
+    assert np.array_equal(vis_hi, vis_lo)
+    return vis_hi
+
+
+def test_planner_matches_golden_fixture():
+    groups, positions, pairs, vis = read_visibility_fixture()
+    plan = pg.pg_pack_host(groups, 4, 2, 64)
+    assert np.array_equal(plan["pos_ids"], positions)
+    assert (plan["pairs"], plan["baseline_pairs"]) == pairs
+    assert np.array_equal(_visibility_from_plan(plan), vis)
+
+
+def _random_groups(rng, max_groups=4, max_p=300, max_r=200, max_g=6):
+    return [(int(rng.integers(0, max_p)),
+             [int(x) for x in rng.integers(0, max_r, size=int(rng.integers(1, max_g + 1)))])
+            for _ in range(int(rng.integers(1, max_groups + 1)))]
+
+
+def test_planner_random_layouts():
+    rng = np.random.default_rng(99)
+    for _ in range(30):
+        groups = _random_groups(rng)
+        plan = pg.pg_pack_host(groups, 8, 2, 128)
+        _, T = member_sequences(groups)
+        assert plan["total_rows"] == T
+        assert np.array_equal(plan["pos_ids"], position_ids(groups))
+        assert (plan["pairs"], plan["baseline_pairs"]) == pair_counts(groups)
+        vis = _visibility_from_plan(plan)
+        assert int(vis.sum()) == plan["pairs"]
+        # query tiles partition the rows, stay in one group, cost-sorted
+        covered = np.zeros(T, dtype=int)
+        costs = []
+        for q0, q1, g0, pe in plan["q_tiles"]:
+            assert 0 < q1 - q0 <= pg.PG_TILE_Q
+            covered[q0:q1] += 1
+            gi = np.searchsorted(plan["group_start"], q0, side="right") - 1
+            assert plan["group_start"][gi] == g0 and plan["prefix_end"][gi] == pe
+            assert q1 <= plan["group_start"][gi + 1]
+            costs.append(int(vis[q0:q1].sum()))
+        assert np.all(covered == 1)
+        assert costs == sorted(costs, reverse=True)
+        # key tiles partition the rows; q_end bounds every query that sees them
+        covered[:] = 0
+        costs = []
+        for k0, k1, qend, pe in plan["kv_tiles"]:
+            assert 0 < k1 - k0 <= pg.PG_TILE_KV
+            covered[k0:k1] += 1
+            seen_by = np.nonzero(vis[:, k0:k1].any(axis=1))[0]
+            assert seen_by.min() >= k0 and seen_by.max() < qend
+            assert seen_by.max() == qend - 1
+            costs.append(int(vis[:, k0:k1].sum()))
+        assert np.all(covered == 1)
+        assert costs == sorted(costs, reverse=True)
+
+
+def test_full_size_layouts_plan():
+    from workloads import attention_workloads
+    for w in attention_workloads().values():
+        groups = [(g.prefix_len, list(g.resp_lens)) for g in w.groups]
+        plan = pg.pg_pack_host(groups, w.num_q_heads, w.num_kv_heads, w.head_dim)
+        assert plan["total_rows"] == w.total_rows
+        assert (plan["pairs"], plan["baseline_pairs"]) == pair_counts(groups)
+
+
+def test_empty_and_degenerate_layouts():
+    plan = pg.pg_pack_host([], 2, 2, 64)
+    assert plan["total_rows"] == 0 and plan["num_q_tiles"] == 0
+    plan = pg.pg_pack_host([(0, [0, 0])], 2, 2, 64)
+    assert plan["total_rows"] == 0 and plan["num_q_tiles"] == 0 and plan["num_kv_tiles"] == 0
+    plan = pg.pg_pack_host([(0, [1])], 2, 1, 128)
+    assert plan["total_rows"] == 1 and plan["pairs"] == 1
+
+
+# ---------------------------------------------------------------- validation
+
+def _groups(groups, hq=4, hkv=2, d=64):
+    return pg._groups_struct(groups, hq, hkv, d)
+
+
+@pytest.mark.parametrize("groups,hq,hkv,d,status", [
+    ([(-1, [3])], 2, 2, 64, pg.PG_ERR_INVALID_ARG),
+    ([(4, [])], 2, 2, 64, pg.PG_ERR_INVALID_ARG),
+    ([(4, [2, -3])], 2, 2, 64, pg.PG_ERR_INVALID_ARG),
+    ([(4, [2])], 3, 2, 64, pg.PG_ERR_INVALID_ARG),
+    ([(4, [2])], 2, 0, 64, pg.PG_ERR_INVALID_ARG),
+    ([(4, [2])], 2, 2, 96, pg.PG_ERR_UNSUPPORTED),
+    ([(4, [2])], 2, 2, 256, pg.PG_ERR_UNSUPPORTED),
+])
+def test_pack_rejects_bad_descriptions(groups, hq, hkv, d, status):
+    L = _lib()
+    g, keep = _groups(groups, hq, hkv, d)
+    assert L.pg_pack_buffer_size(ctypes.byref(g)) == 0
+    buf = np.zeros(1024, dtype=np.int32)
+    desc = pg.PgDesc()
+    st = L.pg_pack_host(ctypes.byref(g), buf.ctypes.data_as(ctypes.c_void_p), buf.nbytes, None,
+                        ctypes.byref(desc))
+    assert st == status
+    assert L.pg_last_error()
+
+
+def test_pack_rejects_small_buffer_and_overflow():
+    L = _lib()
+    g, keep = _groups([(100, [50, 50])])
+    need = L.pg_pack_buffer_size(ctypes.byref(g))
+    buf = np.zeros(need // 4, dtype=np.int32)
+    desc = pg.PgDesc()
+    st = L.pg_pack_host(ctypes.byref(g), buf.ctypes.data_as(ctypes.c_void_p), need - 16, None,
+                        ctypes.byref(desc))
+    assert st == pg.PG_ERR_WORKSPACE
+    g, keep = _groups([(2 ** 30, [2 ** 30])])
+    st = L.pg_pack_host(ctypes.byref(g), buf.ctypes.data_as(ctypes.c_void_p), buf.nbytes, None,
+                        ctypes.byref(desc))
+    assert st == pg.PG_ERR_INVALID_ARG
+    # device pack validates before touching the device
+    st = L.pg_pack(ctypes.byref(g), None, 0, None, ctypes.byref(desc), None)
+    assert st == pg.PG_ERR_INVALID_ARG
+
+
+def _host_desc(groups=((5, [3, 2]),), hq=4, hkv=2, d=64):
+    L = _lib()
+    g, keep = _groups(list(groups), hq, hkv, d)
+    need = L.pg_pack_buffer_size(ctypes.byref(g))
+    buf = np.zeros(need // 4 + 4, dtype=np.int32)
+    desc = pg.PgDesc()
+    assert L.pg_pack_host(ctypes.byref(g), buf.ctypes.data_as(ctypes.c_void_p), buf.nbytes, None,
+                          ctypes.byref(desc)) == pg.PG_OK
+    return desc, buf
+
+
+def test_fwd_bwd_validate_before_launch():
+    """Bad arguments are rejected on the host; nothing is launched (no GPU here)."""
+    L = _lib()
+    desc, buf = _host_desc()
+    p = ctypes.c_void_p(4096)       # aligned, never dereferenced: validation fails first
+    bad = ctypes.c_void_p(4096 + 4)  # misaligned
+    f = ctypes.c_float(0.0)
+    assert L.pg_attn_fwd(None, pg.PG_BF16, f, p, p, p, p, p, None) == pg.PG_ERR_INVALID_ARG
+    assert L.pg_attn_fwd(ctypes.byref(desc), 7, f, p, p, p, p, p, None) == pg.PG_ERR_UNSUPPORTED
+    assert L.pg_attn_fwd(ctypes.byref(desc), pg.PG_BF16, f, None, p, p, p, p, None) == pg.PG_ERR_INVALID_ARG
+    assert "q" in L.pg_last_error().decode()
+    assert L.pg_attn_fwd(ctypes.byref(desc), pg.PG_BF16, f, p, bad, p, p, p, None) == pg.PG_ERR_INVALID_ARG
+    assert "aligned" in L.pg_last_error().decode()
+    ws = L.pg_attn_bwd_workspace_size(ctypes.byref(desc), pg.PG_BF16)
+    assert ws >= desc.num_q_heads * desc.total_rows * 4
+    args = [p] * 10
+    st = L.pg_attn_bwd(ctypes.byref(desc), pg.PG_BF16, f, *args, ws - 1, None)
+    assert st == pg.PG_ERR_WORKSPACE
+    args[9] = None
+    st = L.pg_attn_bwd(ctypes.byref(desc), pg.PG_BF16, f, *args, ws, None)
+    assert st == pg.PG_ERR_INVALID_ARG
+    # a descriptor with an unsupported head size is refused
+    d2 = pg.PgDesc.from_buffer_copy(desc)
+    d2.head_dim = 80
+    assert L.pg_attn_fwd(ctypes.byref(d2), pg.PG_BF16, f, p, p, p, p, p, None) == pg.PG_ERR_UNSUPPORTED
+    d2.head_dim = 64
+    d2.num_kv_heads = 3
+    assert L.pg_attn_fwd(ctypes.byref(d2), pg.PG_BF16, f, p, p, p, p, p, None) == pg.PG_ERR_INVALID_ARG
+    # rope argument checks
+    assert L.pg_rope(ctypes.byref(desc), pg.PG_BF16, p, 2, 63, p, ctypes.c_float(1e4), 0, None) == pg.PG_ERR_INVALID_ARG
+    assert L.pg_rope(ctypes.byref(desc), pg.PG_BF16, p, 2, 64, p, ctypes.c_float(0.5), 0, None) == pg.PG_ERR_INVALID_ARG
+    assert L.pg_rope(ctypes.byref(desc), pg.PG_BF16, p, 2, 64, None, ctypes.c_float(1e4), 0, None) == pg.PG_ERR_INVALID_ARG
+
+
+def test_empty_batch_calls_are_no_ops():
+    L = _lib()
+    desc, buf = _host_desc(groups=((0, [0]),))
+    assert desc.total_rows == 0
+    f = ctypes.c_float(0.0)
+    assert L.pg_attn_fwd(ctypes.byref(desc), pg.PG_BF16, f, None, None, None, None, None, None) == pg.PG_OK
+    assert L.pg_attn_bwd(ctypes.byref(desc), pg.PG_BF16, f, *([None] * 10), 0, None) == pg.PG_OK
+
+
+def test_python_binding_has_no_fallback():
+    """The binding imports neither the oracle nor any CPU path."""
+    src = open(pg.__file__).read()
+    assert "oracle" not in src.replace("no fallback", "")
+    assert "import numpy" in src  # numpy only marshals host arrays for the planner

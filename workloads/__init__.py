@@ -125,12 +125,19 @@ def decoder_workload() -> DecoderWorkload:
 
 
 def round_to_bf16(x: np.ndarray) -> np.ndarray:
-    """Round float32 to the nearest bfloat16 (ties to even); return float32 holding it."""
-    x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    bias = ((u >> 16) & 1) + 0x7FFF
-    r = (((u + bias) >> 16) << 16).astype(np.uint32)
-    return r.view(np.float32)
+    """Round float32 to the nearest bfloat16 (ties to even); return float32 holding it.
+
+    Works in place on a float32 copy, in chunks, with uint32 arithmetic (finite
+    inputs only: standard normal draws never produce NaN or Inf).
+    """
+    out = np.array(x, dtype=np.float32, copy=True, order="C")
+    u = out.reshape(-1).view(np.uint32)
+    step = 1 << 24
+    for s in range(0, u.size, step):
+        c = u[s:s + step]
+        c += ((c >> 16) & 1) + np.uint32(0x7FFF)
+        c &= np.uint32(0xFFFF0000)
+    return out
 
 
 def bf16_bits(x: np.ndarray) -> np.ndarray:
