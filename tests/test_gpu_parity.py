@@ -109,7 +109,11 @@ def _identities(groups, hq, hkv, arrs, out):
     """Exact identities of softmax-attention gradients, per group and kv head.
 
     sum_k dV[k] = sum over the group's rows and the kv head's query heads of dO;
-    sum_k dK[k] = 0;  <dQ, Q> = <dK, K>.  Returned as relative deviations."""
+    sum_k dK[k] = 0;  <dQ, Q> = <dK, K>.  Returned as relative deviations.  The
+    inner-product sums cancel heavily (|sum| is ~1e-3 of sum |terms|), so their
+    deviation is scaled by sum |dQ * Q| + sum |dK * K|: an element-wise
+    relative error e in the gradients moves the difference by at most e times
+    that."""
     rep = hq // hkv
     dq, dk, dv = to_np(out["dq"]), to_np(out["dk"]), to_np(out["dv"])
     res = []
@@ -123,9 +127,9 @@ def _identities(groups, hq, hkv, arrs, out):
             rhs = arrs["do"][sl, hs].astype(np.float64).sum(axis=(0, 1))
             e_v = np.linalg.norm(lhs - rhs) / np.linalg.norm(rhs)
             e_k = np.linalg.norm(dk[sl, hk].sum(axis=0)) / np.linalg.norm(dk[sl, hk])
-            a = float((dq[sl, hs] * arrs["q"][sl, hs]).sum())
-            b = float((dk[sl, hk] * arrs["k"][sl, hk]).sum())
-            e_qk = abs(a - b) / max(abs(a), abs(b))
+            tq = dq[sl, hs] * arrs["q"][sl, hs]
+            tk = dk[sl, hk] * arrs["k"][sl, hk]
+            e_qk = abs(float(tq.sum()) - float(tk.sum())) / float(np.abs(tq).sum() + np.abs(tk).sum())
             res.append((e_v, e_k, e_qk))
         t += n
     return np.array(res)
@@ -163,7 +167,7 @@ def _sampled_check(w, q_heads, kv_heads, key_rows_fn):
     ids = _identities(groups, w.num_q_heads, w.num_kv_heads, arrs, out)
     _say(f"[parity] {w.name}: identity max deviations dV-sum {ids[:, 0].max():.2e}, "
          f"dK-sum {ids[:, 1].max():.2e}, <dQ,Q>-<dK,K> {ids[:, 2].max():.2e}")
-    assert ids[:, 0].max() <= 1e-2 and ids[:, 1].max() <= 2e-2 and ids[:, 2].max() <= 2e-2
+    assert ids[:, 0].max() <= 1e-2 and ids[:, 1].max() <= 2e-2 and ids[:, 2].max() <= 1e-2
     return out
 
 
