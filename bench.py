@@ -57,7 +57,41 @@ def parse(argv=None):
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate CPU time budget of the oracle sample")
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="after the timed steps, run one plain 1 GiB device copy; its "
+                         "FETCH_SIZE/WRITE_SIZE counters calibrate the kernels' HBM traffic")
     return ap.parse_args(argv)
+
+
+# kernel name in the library's timing table -> (profile key, sources it is built from)
+KERNEL_SOURCES = {
+    "fwd": ("fwd_bf16_kernel", ["pg_fwd_bf16.hip"]),
+    "bwd_pre": ("bwd_pre_kernel", ["pg_bwd_bf16.hip"]),
+    "bwd_dkdv": ("dkdv_bf16_kernel", ["pg_bwd_bf16.hip"]),
+    "bwd_dq": ("dq_bf16_kernel", ["pg_bwd_bf16.hip"]),
+}
+
+
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch from the committed counter summary, or None.
+
+    None unless profiles/grouped_attn_<workload>.json holds FETCH_SIZE/WRITE_SIZE
+    figures for this kernel taken from the kernel sources as they are now
+    (their sha256 must match), so a changed kernel never reports stale traffic.
+    """
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"grouped_attn_{workload}.json")
+    if kernel not in KERNEL_SOURCES or not os.path.exists(path):
+        return None
+    key, files = KERNEL_SOURCES[kernel]
+    rec = json.load(open(path)).get("kernels", {}).get(key)
+    if not rec:
+        return None
+    m = hashlib.sha256()
+    for f in files + ["pg_device.h", "pg_internal.h"]:
+        with open(os.path.join(ROOT, "shared_prefix_grouped_amd", "csrc", f), "rb") as fh:
+            m.update(fh.read())
+    return rec["hbm_bytes"] if m.hexdigest() == rec.get("source_sha256") else None
 
 
 def groups_of(w):
@@ -187,14 +221,26 @@ def main(argv=None) -> int:
         achieved = alg / (per_launch[dom] * 1e-3) / 1e12
         peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
         roof = {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": peak,
-                "unit": "TFLOP/s", "frac": achieved / peak, "traffic": None,
+                "unit": "TFLOP/s", "frac": achieved / peak,
+                "traffic": measured_traffic(w.name, dom),
                 "algorithmic_flop_per_launch": alg, "avg_launch_ms": per_launch[dom]}
     else:
         alg = 2 * T * hq * d * esz + T * hq * 4
         achieved = alg / (per_launch[dom] * 1e-3) / 1e9
         roof = {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS, "traffic": None,
+                "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
+                "traffic": measured_traffic(w.name, dom),
                 "algorithmic_bytes_per_launch": alg, "avg_launch_ms": per_launch[dom]}
+
+    if a.traffic_probe:
+        n = (1 << 30) // 2
+        src = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] traffic probe: copied {n * 2} bytes")
+        del src, dst
 
     speed = None
     base_ms = None
