@@ -15,10 +15,9 @@ typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 
-// Score value of a masked (query, key) pair, in the base-2 domain.  Finite, so
-// that a row whose first chunk is entirely masked produces exp2(0) garbage
-// instead of NaN; the garbage is wiped by the exp2(m_old - m_new) = 0 rescale
-// when the row meets its first visible key (every row sees at least itself).
+// Initial running max of a row (base-2 domain).  Finite, so that m - m_new and
+// fma(s, c, -m) never meet inf - inf; masked scores are -inf and give
+// probability exactly 0.
 constexpr float kMasked = -1.0e30f;
 
 // D(32x32, f32) += A(32x16, bf16) * B(16x32, bf16).
@@ -47,6 +46,28 @@ __device__ __forceinline__ constexpr int swap23(int u) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+// One MFMA operand fragment read transposed from a row-major LDS tile
+// T[k][m] (m contiguous, row stride `stride` elements), with gfx950's
+// ds_read_b64_tr_b16.  The lane receives column m0 + lane % 32 and, in its 8
+// slots, rows kb + {0..3, 8..11} + 4 * (lane / 32) -- the same contraction
+// order in which a 32x32 accumulator holds its rows (mfma_row), so the
+// fragment pairs with P^T / dS^T / P / dS taken straight from accumulator
+// registers.
+// The instruction works on 16-lane groups: source lane s of a group supplies
+// the 8-byte chunk at row k + s / 4, columns c + 4 * (s % 4); lane i of the
+// group receives column c + i of rows k .. k + 3 (checked on the GPU).
+__device__ __forceinline__ bf16x8 lds_tr_frag(const bf16 *T, int stride, int kb, int m0, int lane) {
+  const int s = lane & 15;
+  const int col = m0 + 16 * ((lane >> 4) & 1) + 4 * (s & 3);
+  const int row = kb + 4 * (lane >> 5) + (s >> 2);
+  const bf16 *p = T + row * stride + col;
+  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)p);
+  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(p + 8 * stride));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
 
 __device__ __forceinline__ float wave_swap_halves(float x) { return __shfl_xor(x, 32); }
 

@@ -17,7 +17,7 @@
 // 64-key chunk (A = K rows from LDS, B = the wave's Q rows held in registers),
 // so lane l owns query row l % 32 and its softmax statistics are per-lane
 // scalars; P^T then feeds O^T += V^T P^T directly from the accumulator
-// registers, with V stored transposed in LDS.
+// registers, with V read transposed from row-major LDS (ds_read_b64_tr_b16).
 
 #include "pg_device.h"
 #include "pg_internal.h"
@@ -31,21 +31,28 @@ struct FwdCfg {
   static constexpr int NW = BM / 32;    // waves
   static constexpr int NT = NW * 64;    // threads
   static constexpr int BN = 64;         // keys per chunk
-  static constexpr int KS = D + 8;      // LDS row stride of K (elements)
-  static constexpr int VS = BN + 8;     // LDS row stride of V^T (elements)
+  static constexpr int KS = D + 8;      // LDS row stride of K (elements): 16 rows hit 64 banks
+  static constexpr int VS = D + 16;     // LDS row stride of V: the 4 rows of a transposing read
+                                        // land in disjoint banks
   static constexpr int C8 = D / 8;      // 16-byte pieces per row
   static constexpr int LOADS = BN * C8 / NT;
   static_assert(BN * C8 % NT == 0, "chunk must split evenly over the threads");
 };
 
+// A row keeps a stale running max until a chunk raises it by more than
+// kRescale (base-2 units): probabilities then stay below 2^kRescale, and the
+// O rescale runs only when some lane of the wave needs it, which after the
+// first chunks is rare.
+constexpr float kRescale = 8.0f;
+
 template <int D>
-__global__ __launch_bounds__(256) void fwd_bf16_kernel(
+__global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
     const int32_t *__restrict__ q_tiles, const int32_t *__restrict__ row_lo,
     const bf16 *__restrict__ Q, const bf16 *__restrict__ K, const bf16 *__restrict__ V,
     bf16 *__restrict__ O, float *__restrict__ LSE, int T, int Hq, int Hkv, float scale_log2) {
   using C = FwdCfg<D>;
   __shared__ __attribute__((aligned(16))) bf16 sK[C::BN * C::KS];
-  __shared__ __attribute__((aligned(16))) bf16 sVt[D * C::VS];
+  __shared__ __attribute__((aligned(16))) bf16 sV[C::BN * C::VS];
 
   const int tile = blockIdx.x / Hq;
   const int h = blockIdx.x - tile * Hq;
@@ -112,10 +119,7 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(
       const int idx = i * C::NT + tid;
       const int row = idx / C::C8, c8 = idx % C::C8;
       *reinterpret_cast<u32x4 *>(&sK[row * C::KS + c8 * 8]) = kreg[i];
-      const bf16x8 vv = __builtin_bit_cast(bf16x8, vreg[i]);
-      const int col = swap23(row);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) sVt[(c8 * 8 + j) * C::VS + col] = vv[j];
+      *reinterpret_cast<u32x4 *>(&sV[row * C::VS + c8 * 8]) = vreg[i];
     }
   };
   auto chunk_range = [&](int ci, int &c0, int &cend) {
@@ -133,6 +137,8 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(
   for (int nb = 0; nb < D / 32; ++nb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[nb][r] = 0.f;
+  // Running max (base-2, scaled) and partial row sum.  m starts finite and
+  // only grows, so a masked score (-inf) always gives exp2(-inf) = 0 exactly.
   float m = kMasked, l = 0.f;
 
   if (nC > 0) {
@@ -158,6 +164,7 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(
     const bool full = (c0 + C::BN <= cend) && (c0 + C::BN - 1 <= qw0) &&
                       (c0 + C::BN <= pe || c0 >= lo_last);
 
+    // S^T = K Q^T for two 32-key blocks
     f32x16 s[2];
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
@@ -170,53 +177,55 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(
         s[b] = mfma32(a, qf[st], s[b]);
       }
     }
-    float mx = kMasked;
+    if (!full) {
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = c0 + b * 32 + mfma_row(r, hi);
+          const bool ok = key < cend && key <= qrow && (key < pe || key >= lo);
+          s[b][r] = ok ? s[b][r] : -INFINITY;
+        }
+    }
+    float mx = s[0][0];
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = s[b][r] * scale_log2;
-        if (!full) {
-          const int key = c0 + b * 32 + mfma_row(r, hi);
-          const bool ok = key < cend && key <= qrow && (key < pe || key >= lo);
-          x = ok ? x : kMasked;
-        }
-        s[b][r] = x;
-        mx = fmaxf(mx, x);
-      }
-    mx = fmaxf(mx, wave_swap_halves(mx));
-    const float m_new = fmaxf(m, mx);
-    const float alpha = fast_exp2(m - m_new);
-    m = m_new;
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[b][r]);
+    mx = fmaxf(mx, wave_swap_halves(mx)) * scale_log2;
+    if (__builtin_amdgcn_ballot_w64(mx > m + kRescale)) {
+      const float m_new = fmaxf(m, mx);
+      const float alpha = fast_exp2(m - m_new);
+      m = m_new;
+      l *= alpha;
+#pragma unroll
+      for (int nb = 0; nb < D / 32; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[nb][r] *= alpha;
+    }
+    const float neg_m = -m;
     float rs = 0.f;
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = fast_exp2(s[b][r] - m_new);
+        const float p = fast_exp2(fmaf(s[b][r], scale_log2, neg_m));
         s[b][r] = p;
         rs += p;
       }
-    l = l * alpha + rs;
-#pragma unroll
-    for (int nb = 0; nb < D / 32; ++nb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[nb][r] *= alpha;
-    bf16x8 pf[2][2];
+    l += rs;
+    // O^T += V^T P^T: A = V^T read transposed from row-major LDS, B = P^T from registers
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int sub = 0; sub < 2; ++sub) pf[b][sub] = pack8(s[b], sub * 8);
+      for (int sub = 0; sub < 2; ++sub) {
+        const bf16x8 pf = pack8(s[b], sub * 8);
 #pragma unroll
-    for (int nb = 0; nb < D / 32; ++nb)
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int sub = 0; sub < 2; ++sub) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8 *>(
-              &sVt[(nb * 32 + l32) * C::VS + b * 32 + sub * 16 + hi * 8]);
-          o[nb] = mfma32(a, pf[b][sub], o[nb]);
+        for (int nb = 0; nb < D / 32; ++nb) {
+          const bf16x8 a = lds_tr_frag(sV, C::VS, b * 32 + sub * 16, nb * 32, lane);
+          o[nb] = mfma32(a, pf, o[nb]);
         }
+      }
   }
 
   if (!wave_active) return;
