@@ -55,12 +55,11 @@ struct DkdvCfg {
   static constexpr int BN = PG_TILE_KV;  // key rows per workgroup
   static constexpr int NW = BN / 32;     // waves (32 key rows each)
   static constexpr int NT = NW * 64;
-  static constexpr int BM = 32;          // query rows per chunk
-  static constexpr int QS = D + 8;       // LDS stride of row-major Q, dO
-  static constexpr int TS = BM + 8;      // LDS stride of transposed Q^T, dO^T
+  static constexpr int BM = 64;          // query rows per chunk
   static constexpr int C8 = D / 8;
-  static constexpr int LOADS = (BM * C8 + NT - 1) / NT;
+  static constexpr int LOADS = BM * C8 / NT;
   static constexpr int NQB = BM / 32;    // 32-row query blocks per chunk
+  static_assert(BM * C8 % NT == 0, "chunk must split evenly over the threads");
 };
 
 template <int D>
@@ -71,10 +70,10 @@ __global__ __launch_bounds__(256) void dkdv_bf16_kernel(
     bf16 *__restrict__ dK, bf16 *__restrict__ dV, int T, int Hq, int Hkv, float scale_log2,
     float scale) {
   using C = DkdvCfg<D>;
-  __shared__ __attribute__((aligned(16))) bf16 sQ[C::BM * C::QS];
-  __shared__ __attribute__((aligned(16))) bf16 sQt[D * C::TS];
-  __shared__ __attribute__((aligned(16))) bf16 sdO[C::BM * C::QS];
-  __shared__ __attribute__((aligned(16))) bf16 sdOt[D * C::TS];
+  // Q and dO chunks, row-major and swizzled: read as MFMA rows for S = Q K^T
+  // and dP = dO V^T, and transposed for dV^T += dO^T P and dK^T += Q^T dS.
+  __shared__ __attribute__((aligned(16))) bf16 sQ[C::BM * D];
+  __shared__ __attribute__((aligned(16))) bf16 sdO[C::BM * D];
   __shared__ __attribute__((aligned(16))) float sL[C::BM];
   __shared__ __attribute__((aligned(16))) float sDl[C::BM];
 
@@ -144,7 +143,7 @@ __global__ __launch_bounds__(256) void dkdv_bf16_kernel(
       const int idx = i * C::NT + tid;
       const int row = idx / C::C8, c8 = idx % C::C8;
       const int qr = c0 + row;
-      if (idx < C::BM * C::C8 && qr < T) {
+      if (qr < T) {
         const size_t off = (size_t)qr * q_row + (size_t)h * D + c8 * 8;
         qreg[i] = *reinterpret_cast<const u32x4 *>(Q + off);
         oreg[i] = *reinterpret_cast<const u32x4 *>(dO + off);
@@ -166,19 +165,9 @@ __global__ __launch_bounds__(256) void dkdv_bf16_kernel(
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) {
       const int idx = i * C::NT + tid;
-      if (idx < C::BM * C::C8) {
-        const int row = idx / C::C8, c8 = idx % C::C8;
-        *reinterpret_cast<u32x4 *>(&sQ[row * C::QS + c8 * 8]) = qreg[i];
-        *reinterpret_cast<u32x4 *>(&sdO[row * C::QS + c8 * 8]) = oreg[i];
-        const bf16x8 qv = __builtin_bit_cast(bf16x8, qreg[i]);
-        const bf16x8 ov = __builtin_bit_cast(bf16x8, oreg[i]);
-        const int col = swap23(row);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          sQt[(c8 * 8 + j) * C::TS + col] = qv[j];
-          sdOt[(c8 * 8 + j) * C::TS + col] = ov[j];
-        }
-      }
+      const int row = idx / C::C8, c8 = idx % C::C8;
+      *reinterpret_cast<u32x4 *>(&sQ[swz<D>(row, c8 * 8)]) = qreg[i];
+      *reinterpret_cast<u32x4 *>(&sdO[swz<D>(row, c8 * 8)]) = oreg[i];
     }
     if (tid < C::BM)
       sL[tid] = lreg;
@@ -205,10 +194,12 @@ __global__ __launch_bounds__(256) void dkdv_bf16_kernel(
     if (!wave_active) continue;
     if (c0 + C::BM - 1 < kw0) continue;  // every query precedes every key
     if (c0 >= max_hi) continue;          // no key of this wave is seen this far
-    const bool full = (c0 >= kwl) && (c0 + C::BM <= min_hi);
 
 #pragma unroll
     for (int qb = 0; qb < C::NQB; ++qb) {
+      const int cq = c0 + qb * 32;
+      if (cq + 31 < kw0 || cq >= max_hi) continue;  // 32-row block fully masked
+      const bool full = (cq >= kwl) && (cq + 32 <= min_hi);
       f32x16 s, dp;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -217,11 +208,10 @@ __global__ __launch_bounds__(256) void dkdv_bf16_kernel(
       }
 #pragma unroll
       for (int st = 0; st < D / 16; ++st) {
-        const int off = (qb * 32 + l32) * C::QS + st * 16 + hi * 8;
-        s = mfma32(*reinterpret_cast<const bf16x8 *>(&sQ[off]), kf[st], s);
-        dp = mfma32(*reinterpret_cast<const bf16x8 *>(&sdO[off]), vf[st], dp);
+        s = mfma32(lds_row_frag<D>(sQ, qb * 32 + l32, st * 16 + hi * 8), kf[st], s);
+        dp = mfma32(lds_row_frag<D>(sdO, qb * 32 + l32, st * 16 + hi * 8), vf[st], dp);
       }
-      // register r holds query c0 + qb*32 + mfma_row(r, hi); lane column is the key
+      // register r holds query cq + mfma_row(r, hi); the lane's column is its key
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq) {
         const int ql = qb * 32 + rq * 8 + hi * 4;
@@ -230,7 +220,7 @@ __global__ __launch_bounds__(256) void dkdv_bf16_kernel(
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int r = rq * 4 + j;
-          float p = fast_exp2(s[r] * scale_log2 - Lq[j]);
+          float p = fast_exp2(fmaf(s[r], scale_log2, -Lq[j]));
           if (!full) {
             const int qr = c0 + ql + j;
             p = (key <= qr && qr < hik) ? p : 0.f;
@@ -245,9 +235,8 @@ __global__ __launch_bounds__(256) void dkdv_bf16_kernel(
         const bf16x8 db = pack8(dp, sub * 8);
 #pragma unroll
         for (int nb = 0; nb < D / 32; ++nb) {
-          const int off = (nb * 32 + l32) * C::TS + qb * 32 + sub * 16 + hi * 8;
-          dv[nb] = mfma32(*reinterpret_cast<const bf16x8 *>(&sdOt[off]), pb, dv[nb]);
-          dk[nb] = mfma32(*reinterpret_cast<const bf16x8 *>(&sQt[off]), db, dk[nb]);
+          dv[nb] = mfma32(lds_tr_frag_swz<D>(sdO, qb * 32 + sub * 16, nb * 32, lane), pb, dv[nb]);
+          dk[nb] = mfma32(lds_tr_frag_swz<D>(sQ, qb * 32 + sub * 16, nb * 32, lane), db, dk[nb]);
         }
       }
     }
@@ -276,8 +265,6 @@ struct DqCfg {
   static constexpr int NW = BM / 32;
   static constexpr int NT = NW * 64;
   static constexpr int BN = 64;         // keys per chunk
-  static constexpr int KS = D + 8;
-  static constexpr int TS = BN + 8;
   static constexpr int C8 = D / 8;
   static constexpr int LOADS = BN * C8 / NT;
 };
@@ -289,9 +276,10 @@ __global__ __launch_bounds__(256) void dq_bf16_kernel(
     const float *__restrict__ LSE, const float *__restrict__ Delta, const bf16 *__restrict__ dO,
     bf16 *__restrict__ dQ, int T, int Hq, int Hkv, float scale_log2, float scale) {
   using C = DqCfg<D>;
-  __shared__ __attribute__((aligned(16))) bf16 sK[C::BN * C::KS];
-  __shared__ __attribute__((aligned(16))) bf16 sKt[D * C::TS];
-  __shared__ __attribute__((aligned(16))) bf16 sV[C::BN * C::KS];
+  // K and V chunks, row-major and swizzled: K is read as MFMA rows for
+  // S^T = K Q^T and transposed for dQ^T += K^T dS^T; V as rows for dP^T = V dO^T.
+  __shared__ __attribute__((aligned(16))) bf16 sK[C::BN * D];
+  __shared__ __attribute__((aligned(16))) bf16 sV[C::BN * D];
 
   const int tile = blockIdx.x / Hq;
   const int h = blockIdx.x - tile * Hq;
@@ -309,7 +297,7 @@ __global__ __launch_bounds__(256) void dq_bf16_kernel(
   const int lo = row_ok ? row_lo[qrow] : 0;
   const int lo_first = wave_active ? row_lo[qw0] : 0;
   const int lo_last = wave_active ? row_lo[qwl] : 0;
-  const float Lq = row_ok ? LSE[(size_t)h * T + qrow] * kLog2e : 0.f;
+  const float negL = row_ok ? -LSE[(size_t)h * T + qrow] * kLog2e : 0.f;
   const float Dq = row_ok ? Delta[(size_t)h * T + qrow] : 0.f;
 
   bf16x8 qf[D / 16], of[D / 16];
@@ -360,12 +348,8 @@ __global__ __launch_bounds__(256) void dq_bf16_kernel(
     for (int i = 0; i < C::LOADS; ++i) {
       const int idx = i * C::NT + tid;
       const int row = idx / C::C8, c8 = idx % C::C8;
-      *reinterpret_cast<u32x4 *>(&sK[row * C::KS + c8 * 8]) = kreg[i];
-      *reinterpret_cast<u32x4 *>(&sV[row * C::KS + c8 * 8]) = vreg[i];
-      const bf16x8 kv = __builtin_bit_cast(bf16x8, kreg[i]);
-      const int col = swap23(row);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) sKt[(c8 * 8 + j) * C::TS + col] = kv[j];
+      *reinterpret_cast<u32x4 *>(&sK[swz<D>(row, c8 * 8)]) = kreg[i];
+      *reinterpret_cast<u32x4 *>(&sV[swz<D>(row, c8 * 8)]) = vreg[i];
     }
   };
   auto chunk_range = [&](int ci, int &c0, int &cend) {
@@ -417,14 +401,13 @@ __global__ __launch_bounds__(256) void dq_bf16_kernel(
       }
 #pragma unroll
       for (int st = 0; st < D / 16; ++st) {
-        const int off = (b * 32 + l32) * C::KS + st * 16 + hi * 8;
-        s = mfma32(*reinterpret_cast<const bf16x8 *>(&sK[off]), qf[st], s);
-        dp = mfma32(*reinterpret_cast<const bf16x8 *>(&sV[off]), of[st], dp);
+        s = mfma32(lds_row_frag<D>(sK, b * 32 + l32, st * 16 + hi * 8), qf[st], s);
+        dp = mfma32(lds_row_frag<D>(sV, b * 32 + l32, st * 16 + hi * 8), of[st], dp);
       }
-      // register r holds key c0 + b*32 + mfma_row(r, hi); lane column is the query
+      // register r holds key c0 + b*32 + mfma_row(r, hi); the lane's column is its query
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float p = fast_exp2(s[r] * scale_log2 - Lq);
+        float p = fast_exp2(fmaf(s[r], scale_log2, negL));
         if (!full) {
           const int kr = c0 + b * 32 + mfma_row(r, hi);
           const bool ok = kr < cend && kr <= qrow && (kr < pe || kr >= lo);
@@ -436,10 +419,8 @@ __global__ __launch_bounds__(256) void dq_bf16_kernel(
       for (int sub = 0; sub < 2; ++sub) {
         const bf16x8 db = pack8(s, sub * 8);
 #pragma unroll
-        for (int nb = 0; nb < D / 32; ++nb) {
-          const int off = (nb * 32 + l32) * C::TS + b * 32 + sub * 16 + hi * 8;
-          dq[nb] = mfma32(*reinterpret_cast<const bf16x8 *>(&sKt[off]), db, dq[nb]);
-        }
+        for (int nb = 0; nb < D / 32; ++nb)
+          dq[nb] = mfma32(lds_tr_frag_swz<D>(sK, b * 32 + sub * 16, nb * 32, lane), db, dq[nb]);
       }
     }
   }

@@ -69,6 +69,50 @@ __device__ __forceinline__ bf16x8 lds_tr_frag(const bf16 *T, int stride, int kb,
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// Swizzled row-major bf16 tiles in LDS.  A tile of rows with D columns is
+// stored without padding; inside each row the 16-byte chunk c lives at chunk
+// position c ^ swz_chunk(row).  The permutation makes both access patterns of
+// the kernels bank-conflict free (64 banks of 4 bytes):
+//   * MFMA operand rows: 16 consecutive rows read at the same column, 16 bytes
+//     per lane -> 16 distinct chunk positions (swz_chunk is a bijection on 16
+//     consecutive rows);
+//   * transposing reads: 4 consecutive rows (first row a multiple of 4) x 64
+//     contiguous bytes per half-wave -> the 4 rows land in disjoint 64-byte
+//     bank groups (D = 128: swz_chunk varies in bits 2-3 with row % 4; D = 64:
+//     rows of equal parity differ in bit 2).
+template <int D>
+__device__ __forceinline__ int swz_chunk(int r) {
+  static_assert(D == 64 || D == 128, "head_dim 64 or 128");
+  if constexpr (D == 128)
+    return ((r & 3) << 2) | ((r >> 2) & 3);
+  else
+    return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+
+// Element offset of (row r, column c) in a swizzled tile.
+template <int D>
+__device__ __forceinline__ int swz(int r, int c) {
+  return r * D + ((((c >> 3) ^ swz_chunk<D>(r))) << 3) + (c & 7);
+}
+
+// 16-byte MFMA operand row fragment (8 consecutive columns starting at c).
+template <int D>
+__device__ __forceinline__ bf16x8 lds_row_frag(const bf16 *T, int r, int c) {
+  return *reinterpret_cast<const bf16x8 *>(T + swz<D>(r, c));
+}
+
+// lds_tr_frag for a swizzled tile.
+template <int D>
+__device__ __forceinline__ bf16x8 lds_tr_frag_swz(const bf16 *T, int kb, int m0, int lane) {
+  const int s = lane & 15;
+  const int col = m0 + 16 * ((lane >> 4) & 1) + 4 * (s & 3);
+  const int row = kb + 4 * (lane >> 5) + (s >> 2);
+  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(T + swz<D>(row, col)));
+  const bf16x4 hi =
+      __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(T + swz<D>(row + 8, col)));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
 __device__ __forceinline__ float wave_swap_halves(float x) { return __shfl_xor(x, 32); }
 
 // Pack 8 floats (registers r0..r0+7 of a 32x32 result) into bf16x8.

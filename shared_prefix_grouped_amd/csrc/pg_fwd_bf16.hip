@@ -31,9 +31,6 @@ struct FwdCfg {
   static constexpr int NW = BM / 32;    // waves
   static constexpr int NT = NW * 64;    // threads
   static constexpr int BN = 64;         // keys per chunk
-  static constexpr int KS = D + 8;      // LDS row stride of K (elements): 16 rows hit 64 banks
-  static constexpr int VS = D + 16;     // LDS row stride of V: the 4 rows of a transposing read
-                                        // land in disjoint banks
   static constexpr int C8 = D / 8;      // 16-byte pieces per row
   static constexpr int LOADS = BN * C8 / NT;
   static_assert(BN * C8 % NT == 0, "chunk must split evenly over the threads");
@@ -51,8 +48,10 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
     const bf16 *__restrict__ Q, const bf16 *__restrict__ K, const bf16 *__restrict__ V,
     bf16 *__restrict__ O, float *__restrict__ LSE, int T, int Hq, int Hkv, float scale_log2) {
   using C = FwdCfg<D>;
-  __shared__ __attribute__((aligned(16))) bf16 sK[C::BN * C::KS];
-  __shared__ __attribute__((aligned(16))) bf16 sV[C::BN * C::VS];
+  // K and V chunks, row-major and swizzled (see swz): K is read as MFMA rows,
+  // V transposed.
+  __shared__ __attribute__((aligned(16))) bf16 sK[C::BN * D];
+  __shared__ __attribute__((aligned(16))) bf16 sV[C::BN * D];
 
   const int tile = blockIdx.x / Hq;
   const int h = blockIdx.x - tile * Hq;
@@ -118,8 +117,8 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
     for (int i = 0; i < C::LOADS; ++i) {
       const int idx = i * C::NT + tid;
       const int row = idx / C::C8, c8 = idx % C::C8;
-      *reinterpret_cast<u32x4 *>(&sK[row * C::KS + c8 * 8]) = kreg[i];
-      *reinterpret_cast<u32x4 *>(&sV[row * C::VS + c8 * 8]) = vreg[i];
+      *reinterpret_cast<u32x4 *>(&sK[swz<D>(row, c8 * 8)]) = kreg[i];
+      *reinterpret_cast<u32x4 *>(&sV[swz<D>(row, c8 * 8)]) = vreg[i];
     }
   };
   auto chunk_range = [&](int ci, int &c0, int &cend) {
@@ -172,9 +171,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
       for (int r = 0; r < 16; ++r) s[b][r] = 0.f;
 #pragma unroll
       for (int st = 0; st < D / 16; ++st) {
-        const bf16x8 a =
-            *reinterpret_cast<const bf16x8 *>(&sK[(b * 32 + l32) * C::KS + st * 16 + hi * 8]);
-        s[b] = mfma32(a, qf[st], s[b]);
+        s[b] = mfma32(lds_row_frag<D>(sK, b * 32 + l32, st * 16 + hi * 8), qf[st], s[b]);
       }
     }
     if (!full) {
@@ -222,7 +219,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
         const bf16x8 pf = pack8(s[b], sub * 8);
 #pragma unroll
         for (int nb = 0; nb < D / 32; ++nb) {
-          const bf16x8 a = lds_tr_frag(sV, C::VS, b * 32 + sub * 16, nb * 32, lane);
+          const bf16x8 a = lds_tr_frag_swz<D>(sV, b * 32 + sub * 16, nb * 32, lane);
           o[nb] = mfma32(a, pf, o[nb]);
         }
       }
