@@ -56,10 +56,7 @@ struct DkdvCfg {
   static constexpr int NW = BN / 32;     // waves (32 key rows each)
   static constexpr int NT = NW * 64;
   static constexpr int BM = 64;          // query rows per chunk
-  static constexpr int C8 = D / 8;
-  static constexpr int LOADS = BM * C8 / NT;
   static constexpr int NQB = BM / 32;    // 32-row query blocks per chunk
-  static_assert(BM * C8 % NT == 0, "chunk must split evenly over the threads");
 };
 
 template <int D>
@@ -70,19 +67,20 @@ __global__ __launch_bounds__(256) void dkdv_bf16_kernel(
     bf16 *__restrict__ dK, bf16 *__restrict__ dV, int T, int Hq, int Hkv, float scale_log2,
     float scale) {
   using C = DkdvCfg<D>;
-  // Q and dO chunks, row-major and swizzled: read as MFMA rows for S = Q K^T
-  // and dP = dO V^T, and transposed for dV^T += dO^T P and dK^T += Q^T dS.
-  __shared__ __attribute__((aligned(16))) bf16 sQ[C::BM * D];
-  __shared__ __attribute__((aligned(16))) bf16 sdO[C::BM * D];
-  __shared__ __attribute__((aligned(16))) float sL[C::BM];
-  __shared__ __attribute__((aligned(16))) float sDl[C::BM];
+  // Q and dO chunks (+ their LSE and delta), double-buffered, row-major and
+  // swizzled: read as MFMA rows for S = Q K^T and dP = dO V^T, and transposed
+  // for dV^T += dO^T P and dK^T += Q^T dS.
+  __shared__ __attribute__((aligned(16))) bf16 sQ[2 * C::BM * D];
+  __shared__ __attribute__((aligned(16))) bf16 sdO[2 * C::BM * D];
+  __shared__ __attribute__((aligned(16))) float sL[2 * C::BM];
+  __shared__ __attribute__((aligned(16))) float sDl[2 * C::BM];
 
   const int tile = blockIdx.x / Hkv;
   const int hk = blockIdx.x - tile * Hkv;
   const int rep = Hq / Hkv;
   const int k0 = kv_tiles[4 * tile + 0], k1 = kv_tiles[4 * tile + 1];
   const int qend = kv_tiles[4 * tile + 2];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int l32 = lane & 31, hi = lane >> 5;
 
   const int kw0 = k0 + wave * 32;
@@ -130,67 +128,38 @@ __global__ __launch_bounds__(256) void dkdv_bf16_kernel(
   const int nQ = (qend - k0 + C::BM - 1) / C::BM;  // chunks per query head
   const int nC = nQ * rep;
   const size_t q_row = (size_t)Hq * D;
-  u32x4 qreg[C::LOADS], oreg[C::LOADS];
-  float lreg = 0.f;
   auto chunk_of = [&](int ci, int &h, int &c0) {
     const int hh = ci / nQ;
     h = hk * rep + hh;
     c0 = k0 + (ci - hh * nQ) * C::BM;
   };
-  auto load_chunk = [&](int h, int c0) {
-#pragma unroll
-    for (int i = 0; i < C::LOADS; ++i) {
-      const int idx = i * C::NT + tid;
-      const int row = idx / C::C8, c8 = idx % C::C8;
-      const int qr = c0 + row;
-      if (qr < T) {
-        const size_t off = (size_t)qr * q_row + (size_t)h * D + c8 * 8;
-        qreg[i] = *reinterpret_cast<const u32x4 *>(Q + off);
-        oreg[i] = *reinterpret_cast<const u32x4 *>(dO + off);
-      } else {
-        qreg[i] = u32x4{0, 0, 0, 0};
-        oreg[i] = u32x4{0, 0, 0, 0};
-      }
-    }
-    if (tid < 2 * C::BM) {
-      const int row = tid % C::BM;
-      const int qr = c0 + row;
-      if (qr < T)
-        lreg = tid < C::BM ? LSE[(size_t)h * T + qr] * kLog2e : Delta[(size_t)h * T + qr];
-      else
-        lreg = 0.f;
-    }
-  };
-  auto store_chunk = [&]() {
-#pragma unroll
-    for (int i = 0; i < C::LOADS; ++i) {
-      const int idx = i * C::NT + tid;
-      const int row = idx / C::C8, c8 = idx % C::C8;
-      *reinterpret_cast<u32x4 *>(&sQ[swz<D>(row, c8 * 8)]) = qreg[i];
-      *reinterpret_cast<u32x4 *>(&sdO[swz<D>(row, c8 * 8)]) = oreg[i];
-    }
-    if (tid < C::BM)
-      sL[tid] = lreg;
-    else if (tid < 2 * C::BM)
-      sDl[tid - C::BM] = lreg;
-  };
-
-  if (nC > 0) {
+  // chunk ci lives in LDS buffer ci % 2 and is copied one chunk ahead
+  auto issue = [&](int ci) {
     int h, c0;
-    chunk_of(0, h, c0);
-    load_chunk(h, c0);
-  }
+    chunk_of(ci, h, c0);
+    const int b = ci & 1;
+    async_tile_load<D, C::BM, C::NW>(sQ + b * C::BM * D, Q + (size_t)h * D, q_row, c0, T - 1,
+                                     wave, lane);
+    async_tile_load<D, C::BM, C::NW>(sdO + b * C::BM * D, dO + (size_t)h * D, q_row, c0, T - 1,
+                                     wave, lane);
+    if (wave == 0) async_row_load64(sL + b * C::BM, LSE + (size_t)h * T + c0, T - 1 - c0, lane);
+    if (wave == 1) async_row_load64(sDl + b * C::BM, Delta + (size_t)h * T + c0, T - 1 - c0, lane);
+  };
+  static_assert(C::BM == 64, "LSE/delta rows are copied by one wave instruction each");
+  if (nC > 0) issue(0);
   for (int ci = 0; ci < nC; ++ci) {
     int h, c0;
     chunk_of(ci, h, c0);
+    // chunk ci has landed for every wave, and every wave is done reading the
+    // other buffer, which the next copy overwrites
+    wait_async_loads();
     __syncthreads();
-    store_chunk();
-    __syncthreads();
-    if (ci + 1 < nC) {
-      int h2, c2;
-      chunk_of(ci + 1, h2, c2);
-      load_chunk(h2, c2);
-    }
+    if (ci + 1 < nC) issue(ci + 1);
+    const int b = ci & 1;
+    const bf16 *cQ = sQ + b * C::BM * D;
+    const bf16 *cdO = sdO + b * C::BM * D;
+    const float *cL = sL + b * C::BM;
+    const float *cDl = sDl + b * C::BM;
     if (!wave_active) continue;
     if (c0 + C::BM - 1 < kw0) continue;  // every query precedes every key
     if (c0 >= max_hi) continue;          // no key of this wave is seen this far
@@ -208,19 +177,19 @@ __global__ __launch_bounds__(256) void dkdv_bf16_kernel(
       }
 #pragma unroll
       for (int st = 0; st < D / 16; ++st) {
-        s = mfma32(lds_row_frag<D>(sQ, qb * 32 + l32, st * 16 + hi * 8), kf[st], s);
-        dp = mfma32(lds_row_frag<D>(sdO, qb * 32 + l32, st * 16 + hi * 8), vf[st], dp);
+        s = mfma32(lds_row_frag<D>(cQ, qb * 32 + l32, st * 16 + hi * 8), kf[st], s);
+        dp = mfma32(lds_row_frag<D>(cdO, qb * 32 + l32, st * 16 + hi * 8), vf[st], dp);
       }
       // register r holds query cq + mfma_row(r, hi); the lane's column is its key
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq) {
         const int ql = qb * 32 + rq * 8 + hi * 4;
-        const f32x4 Lq = *reinterpret_cast<const f32x4 *>(&sL[ql]);
-        const f32x4 Dq = *reinterpret_cast<const f32x4 *>(&sDl[ql]);
+        const f32x4 Lq = *reinterpret_cast<const f32x4 *>(&cL[ql]);
+        const f32x4 Dq = *reinterpret_cast<const f32x4 *>(&cDl[ql]);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int r = rq * 4 + j;
-          float p = fast_exp2(fmaf(s[r], scale_log2, -Lq[j]));
+          float p = fast_exp2(fmaf(s[r], scale_log2, -Lq[j] * kLog2e));
           if (!full) {
             const int qr = c0 + ql + j;
             p = (key <= qr && qr < hik) ? p : 0.f;
@@ -235,8 +204,8 @@ __global__ __launch_bounds__(256) void dkdv_bf16_kernel(
         const bf16x8 db = pack8(dp, sub * 8);
 #pragma unroll
         for (int nb = 0; nb < D / 32; ++nb) {
-          dv[nb] = mfma32(lds_tr_frag_swz<D>(sdO, qb * 32 + sub * 16, nb * 32, lane), pb, dv[nb]);
-          dk[nb] = mfma32(lds_tr_frag_swz<D>(sQ, qb * 32 + sub * 16, nb * 32, lane), db, dk[nb]);
+          dv[nb] = mfma32(lds_tr_frag_swz<D>(cdO, qb * 32 + sub * 16, nb * 32, lane), pb, dv[nb]);
+          dk[nb] = mfma32(lds_tr_frag_swz<D>(cQ, qb * 32 + sub * 16, nb * 32, lane), db, dk[nb]);
         }
       }
     }
@@ -265,8 +234,6 @@ struct DqCfg {
   static constexpr int NW = BM / 32;
   static constexpr int NT = NW * 64;
   static constexpr int BN = 64;         // keys per chunk
-  static constexpr int C8 = D / 8;
-  static constexpr int LOADS = BN * C8 / NT;
 };
 
 template <int D>
@@ -276,17 +243,18 @@ __global__ __launch_bounds__(256) void dq_bf16_kernel(
     const float *__restrict__ LSE, const float *__restrict__ Delta, const bf16 *__restrict__ dO,
     bf16 *__restrict__ dQ, int T, int Hq, int Hkv, float scale_log2, float scale) {
   using C = DqCfg<D>;
-  // K and V chunks, row-major and swizzled: K is read as MFMA rows for
-  // S^T = K Q^T and transposed for dQ^T += K^T dS^T; V as rows for dP^T = V dO^T.
-  __shared__ __attribute__((aligned(16))) bf16 sK[C::BN * D];
-  __shared__ __attribute__((aligned(16))) bf16 sV[C::BN * D];
+  // K and V chunks, double-buffered, row-major and swizzled: K is read as MFMA
+  // rows for S^T = K Q^T and transposed for dQ^T += K^T dS^T; V as rows for
+  // dP^T = V dO^T.
+  __shared__ __attribute__((aligned(16))) bf16 sK[2 * C::BN * D];
+  __shared__ __attribute__((aligned(16))) bf16 sV[2 * C::BN * D];
 
   const int tile = blockIdx.x / Hq;
   const int h = blockIdx.x - tile * Hq;
   const int hk = h / (Hq / Hkv);
   const int q0 = q_tiles[4 * tile + 0], q1 = q_tiles[4 * tile + 1];
   const int g0 = q_tiles[4 * tile + 2], pe = q_tiles[4 * tile + 3];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int l32 = lane & 31, hi = lane >> 5;
 
   const int qw0 = q0 + wave * 32;
@@ -327,31 +295,6 @@ __global__ __launch_bounds__(256) void dq_bf16_kernel(
   const size_t kv_row = (size_t)Hkv * D;
   const bf16 *Kh = K + (size_t)hk * D;
   const bf16 *Vh = V + (size_t)hk * D;
-  u32x4 kreg[C::LOADS], vreg[C::LOADS];
-  auto load_chunk = [&](int c0) {
-#pragma unroll
-    for (int i = 0; i < C::LOADS; ++i) {
-      const int idx = i * C::NT + tid;
-      const int row = idx / C::C8, c8 = idx % C::C8;
-      const int kr = c0 + row;
-      if (kr < T) {
-        kreg[i] = *reinterpret_cast<const u32x4 *>(Kh + kr * kv_row + c8 * 8);
-        vreg[i] = *reinterpret_cast<const u32x4 *>(Vh + kr * kv_row + c8 * 8);
-      } else {
-        kreg[i] = u32x4{0, 0, 0, 0};
-        vreg[i] = u32x4{0, 0, 0, 0};
-      }
-    }
-  };
-  auto store_chunk = [&]() {
-#pragma unroll
-    for (int i = 0; i < C::LOADS; ++i) {
-      const int idx = i * C::NT + tid;
-      const int row = idx / C::C8, c8 = idx % C::C8;
-      *reinterpret_cast<u32x4 *>(&sK[swz<D>(row, c8 * 8)]) = kreg[i];
-      *reinterpret_cast<u32x4 *>(&sV[swz<D>(row, c8 * 8)]) = vreg[i];
-    }
-  };
   auto chunk_range = [&](int ci, int &c0, int &cend) {
     if (ci < nA) {
       c0 = a0 + ci * C::BN;
@@ -361,6 +304,14 @@ __global__ __launch_bounds__(256) void dq_bf16_kernel(
       cend = b1;
     }
   };
+  // chunk ci lives in LDS buffer ci % 2 and is copied one chunk ahead
+  auto issue = [&](int ci) {
+    int c0, cend;
+    chunk_range(ci, c0, cend);
+    const int buf = (ci & 1) * C::BN * D;
+    async_tile_load<D, C::BN, C::NW>(sK + buf, Kh, kv_row, c0, T - 1, wave, lane);
+    async_tile_load<D, C::BN, C::NW>(sV + buf, Vh, kv_row, c0, T - 1, wave, lane);
+  };
 
   f32x16 dq[D / 32];
 #pragma unroll
@@ -368,22 +319,15 @@ __global__ __launch_bounds__(256) void dq_bf16_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) dq[nb][r] = 0.f;
 
-  if (nC > 0) {
-    int c0, cend;
-    chunk_range(0, c0, cend);
-    load_chunk(c0);
-  }
+  if (nC > 0) issue(0);
   for (int ci = 0; ci < nC; ++ci) {
     int c0, cend;
     chunk_range(ci, c0, cend);
+    wait_async_loads();
     __syncthreads();
-    store_chunk();
-    __syncthreads();
-    if (ci + 1 < nC) {
-      int n0, nend;
-      chunk_range(ci + 1, n0, nend);
-      load_chunk(n0);
-    }
+    if (ci + 1 < nC) issue(ci + 1);
+    const bf16 *cK = sK + (ci & 1) * C::BN * D;
+    const bf16 *cV = sV + (ci & 1) * C::BN * D;
     if (!wave_active) continue;
     const int clast = min(c0 + C::BN, cend) - 1;
     if (c0 > qwl) continue;
@@ -401,8 +345,8 @@ __global__ __launch_bounds__(256) void dq_bf16_kernel(
       }
 #pragma unroll
       for (int st = 0; st < D / 16; ++st) {
-        s = mfma32(lds_row_frag<D>(sK, b * 32 + l32, st * 16 + hi * 8), qf[st], s);
-        dp = mfma32(lds_row_frag<D>(sV, b * 32 + l32, st * 16 + hi * 8), of[st], dp);
+        s = mfma32(lds_row_frag<D>(cK, b * 32 + l32, st * 16 + hi * 8), qf[st], s);
+        dp = mfma32(lds_row_frag<D>(cV, b * 32 + l32, st * 16 + hi * 8), of[st], dp);
       }
       // register r holds key c0 + b*32 + mfma_row(r, hi); the lane's column is its query
 #pragma unroll
@@ -420,7 +364,7 @@ __global__ __launch_bounds__(256) void dq_bf16_kernel(
         const bf16x8 db = pack8(s, sub * 8);
 #pragma unroll
         for (int nb = 0; nb < D / 32; ++nb)
-          dq[nb] = mfma32(lds_tr_frag_swz<D>(sK, b * 32 + sub * 16, nb * 32, lane), db, dq[nb]);
+          dq[nb] = mfma32(lds_tr_frag_swz<D>(cK, b * 32 + sub * 16, nb * 32, lane), db, dq[nb]);
       }
     }
   }

@@ -113,6 +113,60 @@ __device__ __forceinline__ bf16x8 lds_tr_frag_swz(const bf16 *T, int kb, int m0,
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+typedef __attribute__((address_space(3))) char lds_char;
+
+// gfx950 direct global->LDS copies (global_load_lds_dword / _dwordx4): lane i
+// of the wave writes its 4 / 16 bytes at byte 4 i / 16 i of the LDS block
+// whose address is in M0 (checked on the GPU).  They are issued through
+// inline asm so that the compiler does not treat them as aliasing every later
+// LDS read (it would then wait for them before the first read of the *other*
+// buffer and serialise the double buffering).  Completion is tracked by
+// vmcnt: wait_async_loads() before the barrier that publishes the data.
+__device__ __forceinline__ void lds_dma16(const void *g, const void *lds_block) {
+  const uint32_t a = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_char *)lds_block);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(a), "v"(g) : "memory");
+}
+__device__ __forceinline__ void lds_dma4(const void *g, const void *lds_block) {
+  const uint32_t a = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_char *)lds_block);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(a), "v"(g) : "memory");
+}
+
+// Asynchronous copy of rows [r0, r0 + ROWS) of one head of a row-major bf16
+// matrix (D columns at `src`, `row_stride` elements between rows) into a
+// swizzled LDS tile.  One wave instruction moves 1 KB; lane i fetches the
+// global chunk that the swizzle puts at byte 16 i of the block.  Rows past
+// `r_last` are clamped to it (finite data that the caller masks).
+template <int D, int ROWS, int NWAVES>
+__device__ __forceinline__ void async_tile_load(bf16 *tile, const bf16 *src, size_t row_stride,
+                                                int r0, int r_last, int wave, int lane) {
+  constexpr int CPR = D / 8;     // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;  // rows per wave instruction
+  constexpr int NI = ROWS / RPI; // wave instructions per tile
+  static_assert(ROWS % RPI == 0 && NI % NWAVES == 0, "tile must split evenly over the waves");
+#pragma unroll
+  for (int k = 0; k < NI / NWAVES; ++k) {
+    const int i = k * NWAVES + wave;
+    const int row = i * RPI + lane / CPR;
+    const int c = (lane % CPR) ^ swz_chunk<D>(row);
+    const int gr = min(r0 + row, r_last);
+    lds_dma16(src + (size_t)gr * row_stride + c * 8, tile + i * 512);
+  }
+}
+
+// Asynchronous copy of 64 consecutive floats src[min(i, n_last)] (i = 0..63)
+// into dst[0..63] by one wave.
+__device__ __forceinline__ void async_row_load64(float *dst, const float *src, int n_last, int lane) {
+  lds_dma4(src + min(lane, n_last), dst);
+}
+
+// s_waitcnt vmcnt(0), leaving the other counters alone: this wave's global
+// loads, including the direct-to-LDS ones, have completed.
+__device__ __forceinline__ void wait_async_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Index of the calling wave in its workgroup, as a scalar (so that per-wave
+// decisions compile to scalar branches).
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
 __device__ __forceinline__ float wave_swap_halves(float x) { return __shfl_xor(x, 32); }
 
 // Pack 8 floats (registers r0..r0+7 of a 32x32 result) into bf16x8.

@@ -31,9 +31,6 @@ struct FwdCfg {
   static constexpr int NW = BM / 32;    // waves
   static constexpr int NT = NW * 64;    // threads
   static constexpr int BN = 64;         // keys per chunk
-  static constexpr int C8 = D / 8;      // 16-byte pieces per row
-  static constexpr int LOADS = BN * C8 / NT;
-  static_assert(BN * C8 % NT == 0, "chunk must split evenly over the threads");
 };
 
 // A row keeps a stale running max until a chunk raises it by more than
@@ -48,17 +45,17 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
     const bf16 *__restrict__ Q, const bf16 *__restrict__ K, const bf16 *__restrict__ V,
     bf16 *__restrict__ O, float *__restrict__ LSE, int T, int Hq, int Hkv, float scale_log2) {
   using C = FwdCfg<D>;
-  // K and V chunks, row-major and swizzled (see swz): K is read as MFMA rows,
-  // V transposed.
-  __shared__ __attribute__((aligned(16))) bf16 sK[C::BN * D];
-  __shared__ __attribute__((aligned(16))) bf16 sV[C::BN * D];
+  // K and V chunks, double-buffered, row-major and swizzled (see swz): K is
+  // read as MFMA rows, V transposed.
+  __shared__ __attribute__((aligned(16))) bf16 sK[2 * C::BN * D];
+  __shared__ __attribute__((aligned(16))) bf16 sV[2 * C::BN * D];
 
   const int tile = blockIdx.x / Hq;
   const int h = blockIdx.x - tile * Hq;
   const int hk = h / (Hq / Hkv);
   const int q0 = q_tiles[4 * tile + 0], q1 = q_tiles[4 * tile + 1];
   const int g0 = q_tiles[4 * tile + 2], pe = q_tiles[4 * tile + 3];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int l32 = lane & 31, hi = lane >> 5;
 
   const int qw0 = q0 + wave * 32;         // first row of this wave
@@ -96,31 +93,6 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   const size_t kv_row = (size_t)Hkv * D;
   const bf16 *Kh = K + (size_t)hk * D;
   const bf16 *Vh = V + (size_t)hk * D;
-  u32x4 kreg[C::LOADS], vreg[C::LOADS];
-  auto load_chunk = [&](int c0) {
-#pragma unroll
-    for (int i = 0; i < C::LOADS; ++i) {
-      const int idx = i * C::NT + tid;
-      const int row = idx / C::C8, c8 = idx % C::C8;
-      const int key = c0 + row;
-      if (key < T) {
-        kreg[i] = *reinterpret_cast<const u32x4 *>(Kh + key * kv_row + c8 * 8);
-        vreg[i] = *reinterpret_cast<const u32x4 *>(Vh + key * kv_row + c8 * 8);
-      } else {
-        kreg[i] = u32x4{0, 0, 0, 0};
-        vreg[i] = u32x4{0, 0, 0, 0};
-      }
-    }
-  };
-  auto store_chunk = [&]() {
-#pragma unroll
-    for (int i = 0; i < C::LOADS; ++i) {
-      const int idx = i * C::NT + tid;
-      const int row = idx / C::C8, c8 = idx % C::C8;
-      *reinterpret_cast<u32x4 *>(&sK[swz<D>(row, c8 * 8)]) = kreg[i];
-      *reinterpret_cast<u32x4 *>(&sV[swz<D>(row, c8 * 8)]) = vreg[i];
-    }
-  };
   auto chunk_range = [&](int ci, int &c0, int &cend) {
     if (ci < nA) {
       c0 = a0 + ci * C::BN;
@@ -129,6 +101,15 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
       c0 = b0 + (ci - nA) * C::BN;
       cend = b1;
     }
+  };
+  // chunk ci goes to LDS buffer ci % 2, copied asynchronously one chunk ahead
+  // chunk ci lives in LDS buffer ci % 2 and is copied one chunk ahead
+  auto issue = [&](int ci) {
+    int c0, cend;
+    chunk_range(ci, c0, cend);
+    const int buf = (ci & 1) * C::BN * D;
+    async_tile_load<D, C::BN, C::NW>(sK + buf, Kh, kv_row, c0, T - 1, wave, lane);
+    async_tile_load<D, C::BN, C::NW>(sV + buf, Vh, kv_row, c0, T - 1, wave, lane);
   };
 
   f32x16 o[D / 32];
@@ -140,22 +121,17 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   // only grows, so a masked score (-inf) always gives exp2(-inf) = 0 exactly.
   float m = kMasked, l = 0.f;
 
-  if (nC > 0) {
-    int c0, cend;
-    chunk_range(0, c0, cend);
-    load_chunk(c0);
-  }
+  if (nC > 0) issue(0);
   for (int ci = 0; ci < nC; ++ci) {
     int c0, cend;
     chunk_range(ci, c0, cend);
-    __syncthreads();  // LDS reads of the previous chunk are done
-    store_chunk();
+    // chunk ci has landed for every wave, and every wave is done reading the
+    // other buffer, which the next copy overwrites
+    wait_async_loads();
     __syncthreads();
-    if (ci + 1 < nC) {
-      int n0, nend;
-      chunk_range(ci + 1, n0, nend);
-      load_chunk(n0);  // in flight while this chunk is computed
-    }
+    if (ci + 1 < nC) issue(ci + 1);
+    const bf16 *cK = sK + (ci & 1) * C::BN * D;
+    const bf16 *cV = sV + (ci & 1) * C::BN * D;
     if (!wave_active) continue;
     const int clast = min(c0 + C::BN, cend) - 1;
     if (c0 > qwl) continue;                       // every key follows every row
@@ -171,7 +147,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
       for (int r = 0; r < 16; ++r) s[b][r] = 0.f;
 #pragma unroll
       for (int st = 0; st < D / 16; ++st) {
-        s[b] = mfma32(lds_row_frag<D>(sK, b * 32 + l32, st * 16 + hi * 8), qf[st], s[b]);
+        s[b] = mfma32(lds_row_frag<D>(cK, b * 32 + l32, st * 16 + hi * 8), qf[st], s[b]);
       }
     }
     if (!full) {
@@ -219,12 +195,11 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
         const bf16x8 pf = pack8(s[b], sub * 8);
 #pragma unroll
         for (int nb = 0; nb < D / 32; ++nb) {
-          const bf16x8 a = lds_tr_frag_swz<D>(sV, b * 32 + sub * 16, nb * 32, lane);
+          const bf16x8 a = lds_tr_frag_swz<D>(cV, b * 32 + sub * 16, nb * 32, lane);
           o[nb] = mfma32(a, pf, o[nb]);
         }
       }
   }
-
   if (!wave_active) return;
   const float lt = l + wave_swap_halves(l);
   if (!row_ok) return;
