@@ -161,7 +161,8 @@ pg_status pg_pack_host(const pg_groups *g, void *h_buf, size_t buf_bytes, int32_
 pg_status pg_attn_fwd(const pg_desc *d, pg_dtype t, float softmax_scale, const void *q,
                       const void *k, const void *v, void *o, float *lse, void *stream);
 
-/* Bytes of scratch pg_attn_bwd needs: float [Hq, T] for rowsum(dO * O). */
+/* Bytes of scratch pg_attn_bwd needs: two float [Hq, T] arrays, rowsum(dO * O)
+ * and the logsumexp in base 2, each 16-byte aligned. */
 size_t pg_attn_bwd_workspace_size(const pg_desc *d, pg_dtype t);
 
 /* Backward: gradients of sum(O * dO) with respect to Q, K, V, recomputing the

@@ -426,7 +426,8 @@ pg_status pg_attn_fwd(const pg_desc *d, pg_dtype t, float softmax_scale, const v
 size_t pg_attn_bwd_workspace_size(const pg_desc *d, pg_dtype t) {
   (void)t;
   if (check_desc(d) != PG_OK) return 0;
-  return std::max<size_t>(16, align16(size_t(d->num_q_heads) * size_t(d->total_rows) * 4));
+  // delta and the base-2 logsumexp, float [Hq, T] each
+  return std::max<size_t>(16, 2 * align16(size_t(d->num_q_heads) * size_t(d->total_rows) * 4));
 }
 
 pg_status pg_attn_bwd(const pg_desc *d, pg_dtype t, float softmax_scale, const void *q,
@@ -448,16 +449,19 @@ pg_status pg_attn_bwd(const pg_desc *d, pg_dtype t, float softmax_scale, const v
   const float scale = resolve_scale(softmax_scale, p.D);
   hipStream_t s = static_cast<hipStream_t>(stream);
   float *delta = static_cast<float *>(workspace);
-  hipError_t e = timed(PG_KERNEL_BWD_PRE, s, [&] { return pg::launch_bwd_pre(p, t, o, dout, delta, s); });
+  float *lse2 = reinterpret_cast<float *>(static_cast<char *>(workspace) +
+                                          align16(size_t(p.Hq) * size_t(p.T) * 4));
+  hipError_t e = timed(PG_KERNEL_BWD_PRE, s,
+                       [&] { return pg::launch_bwd_pre(p, t, o, dout, lse, delta, lse2, s); });
   if (e != hipSuccess) return hip_status(e, "pg_attn_bwd preprocess launch");
   e = timed(PG_KERNEL_BWD_DKDV, s, [&] {
-    return (t == PG_BF16) ? pg::launch_bwd_dkdv_bf16(p, scale, q, k, v, lse, delta, dout, dk, dv, s)
-                          : pg::launch_bwd_dkdv_f32(p, scale, q, k, v, lse, delta, dout, dk, dv, s);
+    return (t == PG_BF16) ? pg::launch_bwd_dkdv_bf16(p, scale, q, k, v, lse2, delta, dout, dk, dv, s)
+                          : pg::launch_bwd_dkdv_f32(p, scale, q, k, v, lse2, delta, dout, dk, dv, s);
   });
   if (e == hipSuccess)
     e = timed(PG_KERNEL_BWD_DQ, s, [&] {
-      return (t == PG_BF16) ? pg::launch_bwd_dq_bf16(p, scale, q, k, v, lse, delta, dout, dq, s)
-                            : pg::launch_bwd_dq_f32(p, scale, q, k, v, lse, delta, dout, dq, s);
+      return (t == PG_BF16) ? pg::launch_bwd_dq_bf16(p, scale, q, k, v, lse2, delta, dout, dq, s)
+                            : pg::launch_bwd_dq_f32(p, scale, q, k, v, lse2, delta, dout, dq, s);
     });
   return hip_status(e, "pg_attn_bwd launch");
 }

@@ -24,11 +24,14 @@ namespace pg {
 namespace {
 
 // ---------------------------------------------------------------- preprocess
-// delta[h][t] = sum_d dO[t][h][d] * O[t][h][d], in float.
+// delta[h][t] = sum_d dO[t][h][d] * O[t][h][d], in float, and
+// lse2[h][t] = LSE[h][t] * log2(e) (the backward kernels work in base 2).
 template <typename Tin, int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const Tin *__restrict__ O,
                                                       const Tin *__restrict__ dO,
-                                                      float *__restrict__ delta, int T, int Hq) {
+                                                      const float *__restrict__ lse,
+                                                      float *__restrict__ delta,
+                                                      float *__restrict__ lse2, int T, int Hq) {
   constexpr int TPR = D / 8;            // threads per (row, head), 8 elements each
   constexpr int RPB = 256 / TPR;        // (row, head) pairs per block
   const int tid = threadIdx.x;
@@ -46,6 +49,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const Tin *__restrict__ O,
   if (rh < (long long)T * Hq && part == 0) {
     const int t = (int)(rh / Hq), h = (int)(rh % Hq);
     delta[(size_t)h * T + t] = acc;
+    lse2[(size_t)h * T + t] = lse[(size_t)h * T + t] * kLog2e;
   }
 }
 
@@ -63,7 +67,7 @@ template <int D>
 __global__ __launch_bounds__(256) void dkdv_bf16_kernel(
     const int32_t *__restrict__ kv_tiles, const int32_t *__restrict__ row_hi,
     const bf16 *__restrict__ Q, const bf16 *__restrict__ K, const bf16 *__restrict__ V,
-    const float *__restrict__ LSE, const float *__restrict__ Delta, const bf16 *__restrict__ dO,
+    const float *__restrict__ LSE2, const float *__restrict__ Delta, const bf16 *__restrict__ dO,
     bf16 *__restrict__ dK, bf16 *__restrict__ dV, int T, int Hq, int Hkv, float scale_log2,
     float scale) {
   using C = DkdvCfg<D>;
@@ -75,8 +79,8 @@ __global__ __launch_bounds__(256) void dkdv_bf16_kernel(
   __shared__ __attribute__((aligned(16))) float sL[2 * C::BM];
   __shared__ __attribute__((aligned(16))) float sDl[2 * C::BM];
 
-  const int tile = blockIdx.x / Hkv;
-  const int hk = blockIdx.x - tile * Hkv;
+  int tile, hk;
+  xcd_kvhead_work(blockIdx.x, Hkv, tile, hk);
   const int rep = Hq / Hkv;
   const int k0 = kv_tiles[4 * tile + 0], k1 = kv_tiles[4 * tile + 1];
   const int qend = kv_tiles[4 * tile + 2];
@@ -142,7 +146,7 @@ __global__ __launch_bounds__(256) void dkdv_bf16_kernel(
                                      wave, lane);
     async_tile_load<D, C::BM, C::NW>(sdO + b * C::BM * D, dO + (size_t)h * D, q_row, c0, T - 1,
                                      wave, lane);
-    if (wave == 0) async_row_load64(sL + b * C::BM, LSE + (size_t)h * T + c0, T - 1 - c0, lane);
+    if (wave == 0) async_row_load64(sL + b * C::BM, LSE2 + (size_t)h * T + c0, T - 1 - c0, lane);
     if (wave == 1) async_row_load64(sDl + b * C::BM, Delta + (size_t)h * T + c0, T - 1 - c0, lane);
   };
   static_assert(C::BM == 64, "LSE/delta rows are copied by one wave instruction each");
@@ -189,7 +193,7 @@ __global__ __launch_bounds__(256) void dkdv_bf16_kernel(
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int r = rq * 4 + j;
-          float p = fast_exp2(fmaf(s[r], scale_log2, -Lq[j] * kLog2e));
+          float p = fast_exp2(fmaf(s[r], scale_log2, -Lq[j]));
           if (!full) {
             const int qr = c0 + ql + j;
             p = (key <= qr && qr < hik) ? p : 0.f;
@@ -237,10 +241,10 @@ struct DqCfg {
 };
 
 template <int D>
-__global__ __launch_bounds__(256) void dq_bf16_kernel(
+__global__ __launch_bounds__(256, 2) void dq_bf16_kernel(
     const int32_t *__restrict__ q_tiles, const int32_t *__restrict__ row_lo,
     const bf16 *__restrict__ Q, const bf16 *__restrict__ K, const bf16 *__restrict__ V,
-    const float *__restrict__ LSE, const float *__restrict__ Delta, const bf16 *__restrict__ dO,
+    const float *__restrict__ LSE2, const float *__restrict__ Delta, const bf16 *__restrict__ dO,
     bf16 *__restrict__ dQ, int T, int Hq, int Hkv, float scale_log2, float scale) {
   using C = DqCfg<D>;
   // K and V chunks, double-buffered, row-major and swizzled: K is read as MFMA
@@ -249,8 +253,8 @@ __global__ __launch_bounds__(256) void dq_bf16_kernel(
   __shared__ __attribute__((aligned(16))) bf16 sK[2 * C::BN * D];
   __shared__ __attribute__((aligned(16))) bf16 sV[2 * C::BN * D];
 
-  const int tile = blockIdx.x / Hq;
-  const int h = blockIdx.x - tile * Hq;
+  int tile, h;
+  xcd_qhead_work(blockIdx.x, Hq, Hkv, tile, h);
   const int hk = h / (Hq / Hkv);
   const int q0 = q_tiles[4 * tile + 0], q1 = q_tiles[4 * tile + 1];
   const int g0 = q_tiles[4 * tile + 2], pe = q_tiles[4 * tile + 3];
@@ -265,7 +269,7 @@ __global__ __launch_bounds__(256) void dq_bf16_kernel(
   const int lo = row_ok ? row_lo[qrow] : 0;
   const int lo_first = wave_active ? row_lo[qw0] : 0;
   const int lo_last = wave_active ? row_lo[qwl] : 0;
-  const float negL = row_ok ? -LSE[(size_t)h * T + qrow] * kLog2e : 0.f;
+  const float negL = row_ok ? -LSE2[(size_t)h * T + qrow] : 0.f;
   const float Dq = row_ok ? Delta[(size_t)h * T + qrow] : 0.f;
 
   bf16x8 qf[D / 16], of[D / 16];
@@ -385,7 +389,7 @@ __global__ __launch_bounds__(256) void dq_bf16_kernel(
 }  // namespace
 
 hipError_t launch_bwd_pre(const Plan &p, pg_dtype t, const void *o, const void *dout,
-                          float *delta, hipStream_t s) {
+                          const float *lse, float *delta, float *lse2, hipStream_t s) {
   const long long rows = (long long)p.T * p.Hq;
   if (rows == 0) return hipSuccess;
   const int rpb = 256 / (p.D / 8);
@@ -393,17 +397,17 @@ hipError_t launch_bwd_pre(const Plan &p, pg_dtype t, const void *o, const void *
   if (t == PG_BF16) {
     if (p.D == 128)
       hipLaunchKernelGGL((bwd_pre_kernel<__bf16, 128>), grid, block, 0, s, (const __bf16 *)o,
-                         (const __bf16 *)dout, delta, p.T, p.Hq);
+                         (const __bf16 *)dout, lse, delta, lse2, p.T, p.Hq);
     else
       hipLaunchKernelGGL((bwd_pre_kernel<__bf16, 64>), grid, block, 0, s, (const __bf16 *)o,
-                         (const __bf16 *)dout, delta, p.T, p.Hq);
+                         (const __bf16 *)dout, lse, delta, lse2, p.T, p.Hq);
   } else {
     if (p.D == 128)
       hipLaunchKernelGGL((bwd_pre_kernel<float, 128>), grid, block, 0, s, (const float *)o,
-                         (const float *)dout, delta, p.T, p.Hq);
+                         (const float *)dout, lse, delta, lse2, p.T, p.Hq);
     else
       hipLaunchKernelGGL((bwd_pre_kernel<float, 64>), grid, block, 0, s, (const float *)o,
-                         (const float *)dout, delta, p.T, p.Hq);
+                         (const float *)dout, lse, delta, lse2, p.T, p.Hq);
   }
   return hipGetLastError();
 }

@@ -163,6 +163,40 @@ __device__ __forceinline__ void async_row_load64(float *dst, const float *src, i
 // loads, including the direct-to-LDS ones, have completed.
 __device__ __forceinline__ void wait_async_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Work item of a block in a grid of n_tiles x Hq blocks, one per (tile, query
+// head).  Workgroups are dispatched to the 8 XCDs round-robin by block index
+// and each XCD has its own L2; when the kv heads split evenly over the XCDs,
+// all query heads of one kv head are placed on the same XCD, so the K/V rows
+// they share stay in one L2.  Within an XCD, blocks go tile by tile in the
+// planner's (longest-first) order.
+__device__ __forceinline__ void xcd_qhead_work(int bid, int Hq, int Hkv, int &tile, int &h) {
+  if ((Hkv & 7) == 0) {
+    const int rep = Hq / Hkv;
+    const int per = Hq >> 3;  // query heads served by one XCD
+    const int xcd = bid & 7, slot = bid >> 3;
+    tile = slot / per;
+    const int j = slot - tile * per;
+    const int gi = j / rep;
+    h = (xcd + 8 * gi) * rep + (j - gi * rep);
+  } else {
+    tile = bid / Hq;
+    h = bid - tile * Hq;
+  }
+}
+
+// Same for a grid of n_tiles x Hkv blocks, one per (tile, kv head).
+__device__ __forceinline__ void xcd_kvhead_work(int bid, int Hkv, int &tile, int &hk) {
+  if ((Hkv & 7) == 0) {
+    const int per = Hkv >> 3;
+    const int xcd = bid & 7, slot = bid >> 3;
+    tile = slot / per;
+    hk = xcd + 8 * (slot - tile * per);
+  } else {
+    tile = bid / Hkv;
+    hk = bid - tile * Hkv;
+  }
+}
+
 // Index of the calling wave in its workgroup, as a scalar (so that per-wave
 // decisions compile to scalar branches).
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }

@@ -50,8 +50,8 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   __shared__ __attribute__((aligned(16))) bf16 sK[2 * C::BN * D];
   __shared__ __attribute__((aligned(16))) bf16 sV[2 * C::BN * D];
 
-  const int tile = blockIdx.x / Hq;
-  const int h = blockIdx.x - tile * Hq;
+  int tile, h;
+  xcd_qhead_work(blockIdx.x, Hq, Hkv, tile, h);
   const int hk = h / (Hq / Hkv);
   const int q0 = q_tiles[4 * tile + 0], q1 = q_tiles[4 * tile + 1];
   const int g0 = q_tiles[4 * tile + 2], pe = q_tiles[4 * tile + 3];

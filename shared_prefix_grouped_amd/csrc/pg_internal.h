@@ -28,10 +28,12 @@ hipError_t launch_fwd_bf16(const Plan &p, float scale, const void *q, const void
 hipError_t launch_fwd_f32(const Plan &p, float scale, const void *q, const void *k,
                           const void *v, void *o, float *lse, hipStream_t s);
 
-// Backward preprocess: delta[h][t] = sum_d dO[t][h][d] * O[t][h][d] (float).
+// Backward preprocess: delta[h][t] = sum_d dO[t][h][d] * O[t][h][d] (float)
+// and lse2 = LSE * log2(e).
 hipError_t launch_bwd_pre(const Plan &p, pg_dtype t, const void *o, const void *dout,
-                          float *delta, hipStream_t s);
-// dK, dV (key-stationary) and dQ (query-stationary); no atomics.
+                          const float *lse, float *delta, float *lse2, hipStream_t s);
+// dK, dV (key-stationary) and dQ (query-stationary); no atomics.  `lse`
+// here is the base-2 logsumexp written by the preprocess.
 hipError_t launch_bwd_dkdv_bf16(const Plan &p, float scale, const void *q, const void *k,
                                 const void *v, const float *lse, const float *delta,
                                 const void *dout, void *dk, void *dv, hipStream_t s);

@@ -205,13 +205,15 @@ def test_bf16_varlen_2groups_full_size_sampled():
     _sampled_check(w, q_heads=[0, 63], kv_heads=[3], key_rows_fn=keys)
 
 
-def test_deterministic_bitwise():
-    w = scaled_down("det", [(1000, [333, 12, 700]), (64, [500])], "bf16", 8, 2, 128, seed=5)
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("f32", 128), ("f32", 64)])
+def test_deterministic_bitwise(dtype, d):
+    w = scaled_down("det", [(1000, [333, 12, 700]), (64, [500])], dtype, 8, 2, d, seed=5)
     groups = _groups_of(w)
     arrs = draw_attention_inputs(w)
-    a = run_gpu(groups, 8, 2, 128, arrs, torch.bfloat16)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    a = run_gpu(groups, 8, 2, d, arrs, tdt)
     junk = torch.randn(1 << 22, device="cuda")  # perturb allocator and stream state
-    b = run_gpu(groups, 8, 2, 128, arrs, torch.bfloat16)
+    b = run_gpu(groups, 8, 2, d, arrs, tdt)
     del junk
     for key in ("o", "lse", "dq", "dk", "dv"):
         assert torch.equal(a[key], b[key]), key
