@@ -10,7 +10,7 @@
 //   * dkdv: key-stationary.  A workgroup owns 128 key rows of one key/value
 //     head and walks, in a fixed order, every query head of that kv head and
 //     every 64-row query chunk in [k0, q_end), accumulating dK^T and dV^T in
-//     registers.  For a prefix tile that walk covers the prefix rows and all
+//     registers (split over two waves per 32-key group, see below).  For a prefix tile that walk covers the prefix rows and all
 //     responses of the group, so the group reduction of Lemma 2.1 happens in
 //     registers, in a fixed order.
 //   * dq: query-stationary, over the same two key segments as the forward.
@@ -54,30 +54,41 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const Tin *__restrict__ O,
 }
 
 // ---------------------------------------------------------------- dK, dV
+// A workgroup owns 128 key rows of one kv head, as 4 groups of 32 keys, and
+// runs 8 waves: for each key group, wave A computes S = Q K^T, P and
+// dV^T += dO^T P, and wave B computes dP = dO V^T, dS = P * (dP - delta) and
+// dK^T += Q^T dS, receiving P (fp32) from wave A through LDS.  Each wave then
+// holds one accumulator set and one K or V operand set, so two waves fit on
+// a SIMD and one's softmax arithmetic overlaps the other's matrix work.
 template <int D>
 struct DkdvCfg {
   static constexpr int BN = PG_TILE_KV;  // key rows per workgroup
-  static constexpr int NW = BN / 32;     // waves (32 key rows each)
+  static constexpr int NG = BN / 32;     // 32-key groups
+  static constexpr int NW = 2 * NG;      // waves: role A and role B per key group
   static constexpr int NT = NW * 64;
   static constexpr int BM = 64;          // query rows per chunk
   static constexpr int NQB = BM / 32;    // 32-row query blocks per chunk
 };
 
 template <int D>
-__global__ __launch_bounds__(256) void dkdv_bf16_kernel(
+__global__ __launch_bounds__(512) void dkdv_bf16_kernel(
     const int32_t *__restrict__ kv_tiles, const int32_t *__restrict__ row_hi,
     const bf16 *__restrict__ Q, const bf16 *__restrict__ K, const bf16 *__restrict__ V,
     const float *__restrict__ LSE2, const float *__restrict__ Delta, const bf16 *__restrict__ dO,
     bf16 *__restrict__ dK, bf16 *__restrict__ dV, int T, int Hq, int Hkv, float scale_log2,
     float scale) {
   using C = DkdvCfg<D>;
-  // Q and dO chunks (+ their LSE and delta), double-buffered, row-major and
-  // swizzled: read as MFMA rows for S = Q K^T and dP = dO V^T, and transposed
-  // for dV^T += dO^T P and dK^T += Q^T dS.
+  static_assert(C::NQB == 2, "the P hand-off below is double-buffered by query block parity");
+  // Q and dO chunks (+ their base-2 LSE and delta), double-buffered, row-major
+  // and swizzled: read as MFMA rows for S = Q K^T and dP = dO V^T, and
+  // transposed for dV^T += dO^T P and dK^T += Q^T dS.
   __shared__ __attribute__((aligned(16))) bf16 sQ[2 * C::BM * D];
   __shared__ __attribute__((aligned(16))) bf16 sdO[2 * C::BM * D];
   __shared__ __attribute__((aligned(16))) float sL[2 * C::BM];
   __shared__ __attribute__((aligned(16))) float sDl[2 * C::BM];
+  // P of one 32x32 block per key group, by query-block parity, in the
+  // accumulator layout: [group][parity][register quad][lane].
+  __shared__ __attribute__((aligned(16))) f32x4 sP[C::NG][2][4][64];
 
   int tile, hk;
   xcd_kvhead_work(blockIdx.x, Hkv, tile, hk);
@@ -86,14 +97,16 @@ __global__ __launch_bounds__(256) void dkdv_bf16_kernel(
   const int qend = kv_tiles[4 * tile + 2];
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int l32 = lane & 31, hi = lane >> 5;
+  const bool roleA = wave < C::NG;        // S, P, dV   (else dP, dS, dK)
+  const int kg = roleA ? wave : wave - C::NG;
 
-  const int kw0 = k0 + wave * 32;
+  const int kw0 = k0 + kg * 32;
   const int kwl = min(k1, kw0 + 32) - 1;
-  const bool wave_active = kw0 < k1;
+  const bool group_active = kw0 < k1;
   const int key = kw0 + l32;
   const bool key_ok = key < k1;
   const int hik = key_ok ? row_hi[key] : 0;  // queries [key, hik) see this key
-  // smallest / largest visibility end over the wave's keys
+  // smallest / largest visibility end over the group's keys
   int min_hi = key_ok ? hik : 0x7fffffff, max_hi = hik;
 #pragma unroll
   for (int w = 32; w >= 1; w >>= 1) {
@@ -101,33 +114,29 @@ __global__ __launch_bounds__(256) void dkdv_bf16_kernel(
     max_hi = max(max_hi, __shfl_xor(max_hi, w));
   }
 
-  // K and V rows of this wave as MFMA B operands: column = key l32, k = d.
-  bf16x8 kf[D / 16], vf[D / 16];
+  // K (role A) or V (role B) rows of the group as MFMA B operands:
+  // column = key l32, k = d.
+  bf16x8 kvf[D / 16];
   {
-    const size_t base = ((size_t)key * Hkv + hk) * D + 8 * hi;
+    const bf16 *src = (roleA ? K : V) + ((size_t)key * Hkv + hk) * D + 8 * hi;
 #pragma unroll
     for (int st = 0; st < D / 16; ++st) {
       if (key_ok) {
-        kf[st] = *reinterpret_cast<const bf16x8 *>(K + base + 16 * st);
-        vf[st] = *reinterpret_cast<const bf16x8 *>(V + base + 16 * st);
+        kvf[st] = *reinterpret_cast<const bf16x8 *>(src + 16 * st);
       } else {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          kf[st][j] = (__bf16)0.f;
-          vf[st][j] = (__bf16)0.f;
-        }
+        for (int j = 0; j < 8; ++j) kvf[st][j] = (__bf16)0.f;
       }
     }
   }
 
-  f32x16 dk[D / 32], dv[D / 32];
+  // dV^T (role A) or dK^T (role B): register r of lane l holds
+  // d = 32 nb + mfma_row(r, hi), key = l32.
+  f32x16 acc[D / 32];
 #pragma unroll
   for (int nb = 0; nb < D / 32; ++nb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      dk[nb][r] = 0.f;
-      dv[nb][r] = 0.f;
-    }
+    for (int r = 0; r < 16; ++r) acc[nb][r] = 0.f;
 
   const int nQ = (qend - k0 + C::BM - 1) / C::BM;  // chunks per query head
   const int nC = nQ * rep;
@@ -150,84 +159,148 @@ __global__ __launch_bounds__(256) void dkdv_bf16_kernel(
     if (wave == 1) async_row_load64(sDl + b * C::BM, Delta + (size_t)h * T + c0, T - 1 - c0, lane);
   };
   static_assert(C::BM == 64, "LSE/delta rows are copied by one wave instruction each");
-  if (nC > 0) issue(0);
-  for (int ci = 0; ci < nC; ++ci) {
-    int h, c0;
-    chunk_of(ci, h, c0);
-    // chunk ci has landed for every wave, and every wave is done reading the
-    // other buffer, which the next copy overwrites
-    wait_async_loads();
-    __syncthreads();
-    if (ci + 1 < nC) issue(ci + 1);
-    const int b = ci & 1;
-    const bf16 *cQ = sQ + b * C::BM * D;
-    const bf16 *cdO = sdO + b * C::BM * D;
-    const float *cL = sL + b * C::BM;
-    const float *cDl = sDl + b * C::BM;
-    if (!wave_active) continue;
-    if (c0 + C::BM - 1 < kw0) continue;  // every query precedes every key
-    if (c0 >= max_hi) continue;          // no key of this wave is seen this far
 
+  // Whether query block qb of chunk c0 meets the group's keys at all, and
+  // whether every (query, key) pair of it is visible.
+  auto block_live = [&](int c0, int qb) {
+    const int cq = c0 + qb * 32;
+    return group_active && !(cq + 31 < kw0 || cq >= max_hi);
+  };
+  auto block_full = [&](int c0, int qb) {
+    const int cq = c0 + qb * 32;
+    return (cq >= kwl) && (cq + 32 <= min_hi);
+  };
+
+  // Role A: S -> P for query block qb; P (fp32) goes to LDS for role B and,
+  // packed to bf16, stays in registers for dV.
+  auto a_scores = [&](const bf16 *cQ, const float *cL, int c0, int qb, bf16x8 (&pk)[2]) {
+    f32x16 s;
 #pragma unroll
-    for (int qb = 0; qb < C::NQB; ++qb) {
-      const int cq = c0 + qb * 32;
-      if (cq + 31 < kw0 || cq >= max_hi) continue;  // 32-row block fully masked
-      const bool full = (cq >= kwl) && (cq + 32 <= min_hi);
-      f32x16 s, dp;
+    for (int r = 0; r < 16; ++r) s[r] = 0.f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[r] = 0.f;
-        dp[r] = 0.f;
-      }
+    for (int st = 0; st < D / 16; ++st)
+      s = mfma32(lds_row_frag<D>(cQ, qb * 32 + l32, st * 16 + hi * 8), kvf[st], s);
+    const bool full = block_full(c0, qb);
 #pragma unroll
-      for (int st = 0; st < D / 16; ++st) {
-        s = mfma32(lds_row_frag<D>(cQ, qb * 32 + l32, st * 16 + hi * 8), kf[st], s);
-        dp = mfma32(lds_row_frag<D>(cdO, qb * 32 + l32, st * 16 + hi * 8), vf[st], dp);
-      }
-      // register r holds query cq + mfma_row(r, hi); the lane's column is its key
+    for (int rq = 0; rq < 4; ++rq) {
+      const int ql = qb * 32 + rq * 8 + hi * 4;
+      const f32x4 Lq = *reinterpret_cast<const f32x4 *>(&cL[ql]);
+      f32x4 pq;
 #pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        const int ql = qb * 32 + rq * 8 + hi * 4;
-        const f32x4 Lq = *reinterpret_cast<const f32x4 *>(&cL[ql]);
-        const f32x4 Dq = *reinterpret_cast<const f32x4 *>(&cDl[ql]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int r = rq * 4 + j;
-          float p = fast_exp2(fmaf(s[r], scale_log2, -Lq[j]));
-          if (!full) {
-            const int qr = c0 + ql + j;
-            p = (key <= qr && qr < hik) ? p : 0.f;
-          }
-          s[r] = p;
-          dp[r] = p * (dp[r] - Dq[j]);
+      for (int j = 0; j < 4; ++j) {
+        float p = fast_exp2(fmaf(s[rq * 4 + j], scale_log2, -Lq[j]));
+        if (!full) {
+          const int qr = c0 + ql + j;
+          p = (key <= qr && qr < hik) ? p : 0.f;
         }
+        s[rq * 4 + j] = p;
+        pq[j] = p;
       }
+      sP[kg][qb & 1][rq][lane] = pq;
+    }
+    pk[0] = pack8(s, 0);
+    pk[1] = pack8(s, 8);
+  };
+  // Role A: dV^T += dO^T P
+  auto a_dv = [&](const bf16 *cdO, int qb, const bf16x8 (&pk)[2]) {
 #pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
-        const bf16x8 pb = pack8(s, sub * 8);
-        const bf16x8 db = pack8(dp, sub * 8);
+    for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-        for (int nb = 0; nb < D / 32; ++nb) {
-          dv[nb] = mfma32(lds_tr_frag_swz<D>(cdO, qb * 32 + sub * 16, nb * 32, lane), pb, dv[nb]);
-          dk[nb] = mfma32(lds_tr_frag_swz<D>(cQ, qb * 32 + sub * 16, nb * 32, lane), db, dk[nb]);
-        }
-      }
+      for (int nb = 0; nb < D / 32; ++nb)
+        acc[nb] = mfma32(lds_tr_frag_swz<D>(cdO, qb * 32 + sub * 16, nb * 32, lane), pk[sub], acc[nb]);
+  };
+  // Role B: dP = dO V^T for query block qb
+  auto b_dp = [&](const bf16 *cdO, int qb, f32x16 &dp) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dp[r] = 0.f;
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st)
+      dp = mfma32(lds_row_frag<D>(cdO, qb * 32 + l32, st * 16 + hi * 8), kvf[st], dp);
+  };
+  // Role B: dS = P * (dP - delta), dK^T += Q^T dS
+  auto b_dk = [&](const bf16 *cQ, const float *cDl, int qb, f32x16 &dp) {
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq) {
+      const int ql = qb * 32 + rq * 8 + hi * 4;
+      const f32x4 Dq = *reinterpret_cast<const f32x4 *>(&cDl[ql]);
+      const f32x4 pq = sP[kg][qb & 1][rq][lane];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dp[rq * 4 + j] = pq[j] * (dp[rq * 4 + j] - Dq[j]);
+    }
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const bf16x8 db = pack8(dp, sub * 8);
+#pragma unroll
+      for (int nb = 0; nb < D / 32; ++nb)
+        acc[nb] = mfma32(lds_tr_frag_swz<D>(cQ, qb * 32 + sub * 16, nb * 32, lane), db, acc[nb]);
+    }
+  };
+
+  // Both roles run the same sequence of chunks and barriers (three per
+  // chunk); the role is chosen once, outside the loop, so that each wave's
+  // registers hold only its own role's state across the barriers.
+  auto chunk_buffers = [&](int ci, const bf16 *&cQ, const bf16 *&cdO, const float *&cL,
+                           const float *&cDl) {
+    const int b = ci & 1;
+    cQ = sQ + b * C::BM * D;
+    cdO = sdO + b * C::BM * D;
+    cL = sL + b * C::BM;
+    cDl = sDl + b * C::BM;
+  };
+  if (nC > 0) issue(0);
+  if (roleA) {
+    for (int ci = 0; ci < nC; ++ci) {
+      int h, c0;
+      chunk_of(ci, h, c0);
+      // chunk ci has landed for every wave, and every wave is done reading
+      // the other buffer, which the next copy overwrites
+      wait_async_loads();
+      __syncthreads();
+      if (ci + 1 < nC) issue(ci + 1);
+      const bf16 *cQ, *cdO;
+      const float *cL, *cDl;
+      chunk_buffers(ci, cQ, cdO, cL, cDl);
+      const bool live0 = block_live(c0, 0), live1 = block_live(c0, 1);
+      bf16x8 pk0[2], pk1[2];
+      if (live0) a_scores(cQ, cL, c0, 0, pk0);
+      __syncthreads();  // P of block 0 is in LDS
+      if (live0) a_dv(cdO, 0, pk0);
+      if (live1) a_scores(cQ, cL, c0, 1, pk1);
+      __syncthreads();  // P of block 1 is in LDS
+      if (live1) a_dv(cdO, 1, pk1);
+    }
+  } else {
+    for (int ci = 0; ci < nC; ++ci) {
+      int h, c0;
+      chunk_of(ci, h, c0);
+      wait_async_loads();
+      __syncthreads();
+      if (ci + 1 < nC) issue(ci + 1);
+      const bf16 *cQ, *cdO;
+      const float *cL, *cDl;
+      chunk_buffers(ci, cQ, cdO, cL, cDl);
+      const bool live0 = block_live(c0, 0), live1 = block_live(c0, 1);
+      f32x16 dp0, dp1;
+      if (live0) b_dp(cdO, 0, dp0);
+      __syncthreads();  // P of block 0 is in LDS
+      if (live0) b_dk(cQ, cDl, 0, dp0);
+      if (live1) b_dp(cdO, 1, dp1);
+      __syncthreads();  // P of block 1 is in LDS
+      if (live1) b_dk(cQ, cDl, 1, dp1);
     }
   }
 
-  if (!wave_active || !key_ok) return;
-  bf16 *dkp = dK + ((size_t)key * Hkv + hk) * D;
-  bf16 *dvp = dV + ((size_t)key * Hkv + hk) * D;
+  if (!group_active || !key_ok) return;
+  bf16 *dst = (roleA ? dV : dK) + ((size_t)key * Hkv + hk) * D;
+  const float f = roleA ? 1.f : scale;
 #pragma unroll
   for (int nb = 0; nb < D / 32; ++nb)
 #pragma unroll
     for (int rq = 0; rq < 4; ++rq) {
       const int d0 = nb * 32 + rq * 8 + hi * 4;
-      *reinterpret_cast<u32x2 *>(dkp + d0) =
-          pack4_bf16(dk[nb][rq * 4 + 0] * scale, dk[nb][rq * 4 + 1] * scale,
-                     dk[nb][rq * 4 + 2] * scale, dk[nb][rq * 4 + 3] * scale);
-      *reinterpret_cast<u32x2 *>(dvp + d0) =
-          pack4_bf16(dv[nb][rq * 4 + 0], dv[nb][rq * 4 + 1], dv[nb][rq * 4 + 2], dv[nb][rq * 4 + 3]);
+      *reinterpret_cast<u32x2 *>(dst + d0) =
+          pack4_bf16(acc[nb][rq * 4 + 0] * f, acc[nb][rq * 4 + 1] * f, acc[nb][rq * 4 + 2] * f,
+                     acc[nb][rq * 4 + 3] * f);
     }
 }
 
@@ -416,7 +489,7 @@ hipError_t launch_bwd_dkdv_bf16(const Plan &p, float scale, const void *q, const
                                 const void *v, const float *lse, const float *delta,
                                 const void *dout, void *dk, void *dv, hipStream_t s) {
   if (p.n_kv_tiles == 0) return hipSuccess;
-  const dim3 grid((unsigned)p.n_kv_tiles * (unsigned)p.Hkv), block(256);
+  const dim3 grid((unsigned)p.n_kv_tiles * (unsigned)p.Hkv), block(DkdvCfg<128>::NT);
   const float sl2 = scale * kLog2e;
   if (p.D == 128)
     hipLaunchKernelGGL(dkdv_bf16_kernel<128>, grid, block, 0, s, p.kv_tiles, p.row_hi,
