@@ -147,14 +147,16 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
     c0 = k0 + (ci - hh * nQ) * C::BM;
   };
   // chunk ci lives in LDS buffer ci % 2 and is copied one chunk ahead
+  TileCopy<D, C::BM, C::NW> copy;
+  copy.init(q_row, wave, lane);
+  const uint32_t sQ_lds = lds_address(sQ), sdO_lds = lds_address(sdO);
   auto issue = [&](int ci) {
     int h, c0;
     chunk_of(ci, h, c0);
     const int b = ci & 1;
-    async_tile_load<D, C::BM, C::NW>(sQ + b * C::BM * D, Q + (size_t)h * D, q_row, c0, T - 1,
-                                     wave, lane);
-    async_tile_load<D, C::BM, C::NW>(sdO + b * C::BM * D, dO + (size_t)h * D, q_row, c0, T - 1,
-                                     wave, lane);
+    const int buf = b * C::BM * D;
+    copy.issue(sQ + buf, sQ_lds + 2 * buf, Q + (size_t)h * D, q_row, c0, T - 1, wave, lane);
+    copy.issue(sdO + buf, sdO_lds + 2 * buf, dO + (size_t)h * D, q_row, c0, T - 1, wave, lane);
     if (wave == 0) async_row_load64(sL + b * C::BM, LSE2 + (size_t)h * T + c0, T - 1 - c0, lane);
     if (wave == 1) async_row_load64(sDl + b * C::BM, Delta + (size_t)h * T + c0, T - 1 - c0, lane);
   };
@@ -382,12 +384,15 @@ __global__ __launch_bounds__(256, 2) void dq_bf16_kernel(
     }
   };
   // chunk ci lives in LDS buffer ci % 2 and is copied one chunk ahead
+  TileCopy<D, C::BN, C::NW> copy;
+  copy.init(kv_row, wave, lane);
+  const uint32_t sK_lds = lds_address(sK), sV_lds = lds_address(sV);
   auto issue = [&](int ci) {
     int c0, cend;
     chunk_range(ci, c0, cend);
     const int buf = (ci & 1) * C::BN * D;
-    async_tile_load<D, C::BN, C::NW>(sK + buf, Kh, kv_row, c0, T - 1, wave, lane);
-    async_tile_load<D, C::BN, C::NW>(sV + buf, Vh, kv_row, c0, T - 1, wave, lane);
+    copy.issue(sK + buf, sK_lds + 2 * buf, Kh, kv_row, c0, T - 1, wave, lane);
+    copy.issue(sV + buf, sV_lds + 2 * buf, Vh, kv_row, c0, T - 1, wave, lane);
   };
 
   f32x16 dq[D / 32];

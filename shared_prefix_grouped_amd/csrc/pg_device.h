@@ -153,6 +153,54 @@ __device__ __forceinline__ void async_tile_load(bf16 *tile, const bf16 *src, siz
   }
 }
 
+// The same copy as async_tile_load with addressing hoisted out of the chunk
+// loop: each lane's byte offset inside a tile (row * row stride + swizzled
+// chunk) is computed once, and an in-bounds tile is copied with the
+// scalar-base form of the instruction (64-bit base in SGPRs + 32-bit lane
+// offset), so the per-chunk cost is scalar arithmetic only.  Tiles that reach
+// past the last row take the clamped per-lane path of async_tile_load.
+template <int D, int ROWS, int NWAVES>
+struct TileCopy {
+  static constexpr int CPR = D / 8;
+  static constexpr int RPI = 64 / CPR;
+  static constexpr int NI = ROWS / RPI;
+  static constexpr int PER_WAVE = NI / NWAVES;
+  static_assert(ROWS % RPI == 0 && NI % NWAVES == 0, "tile must split evenly over the waves");
+  uint32_t voff[PER_WAVE];
+
+  __device__ __forceinline__ void init(size_t row_stride, int wave, int lane) {
+#pragma unroll
+    for (int k = 0; k < PER_WAVE; ++k) {
+      const int i = k * NWAVES + wave;
+      const int row = i * RPI + lane / CPR;
+      const int c = (lane % CPR) ^ swz_chunk<D>(row);
+      voff[k] = (uint32_t)(row * row_stride * sizeof(bf16) + c * 16);
+    }
+  }
+
+  // rows [r0, r0 + ROWS) of src (one head, `row_stride` elements per row)
+  // into `tile`, whose LDS byte address is `tile_lds` (see lds_address)
+  __device__ __forceinline__ void issue(bf16 *tile, uint32_t tile_lds, const bf16 *src,
+                                        size_t row_stride, int r0, int r_last, int wave,
+                                        int lane) const {
+    if (r0 + ROWS - 1 <= r_last) {
+      const uint64_t base = (uint64_t)(uintptr_t)(src + (size_t)r0 * row_stride);
+      const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)base);
+      const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
+      const uint64_t sbase = ((uint64_t)hi << 32) | lo;
+#pragma unroll
+      for (int k = 0; k < PER_WAVE; ++k) {
+        const uint32_t a = tile_lds + (uint32_t)((k * NWAVES + wave) * 1024);
+        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(a), "v"(voff[k]),
+                     "s"(sbase)
+                     : "memory");
+      }
+    } else {
+      async_tile_load<D, ROWS, NWAVES>(tile, src, row_stride, r0, r_last, wave, lane);
+    }
+  }
+};
+
 // Asynchronous copy of 64 consecutive floats src[min(i, n_last)] (i = 0..63)
 // into dst[0..63] by one wave.
 __device__ __forceinline__ void async_row_load64(float *dst, const float *src, int n_last, int lane) {
@@ -195,6 +243,11 @@ __device__ __forceinline__ void xcd_kvhead_work(int bid, int Hkv, int &tile, int
     tile = bid / Hkv;
     hk = bid - tile * Hkv;
   }
+}
+
+// Byte address of an LDS array in the LDS aperture (for M0), as a scalar.
+__device__ __forceinline__ uint32_t lds_address(const void *p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_char *)p);
 }
 
 // Index of the calling wave in its workgroup, as a scalar (so that per-wave

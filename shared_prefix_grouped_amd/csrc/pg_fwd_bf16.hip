@@ -104,12 +104,15 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   };
   // chunk ci goes to LDS buffer ci % 2, copied asynchronously one chunk ahead
   // chunk ci lives in LDS buffer ci % 2 and is copied one chunk ahead
+  TileCopy<D, C::BN, C::NW> copy;
+  copy.init(kv_row, wave, lane);
+  const uint32_t sK_lds = lds_address(sK), sV_lds = lds_address(sV);
   auto issue = [&](int ci) {
     int c0, cend;
     chunk_range(ci, c0, cend);
     const int buf = (ci & 1) * C::BN * D;
-    async_tile_load<D, C::BN, C::NW>(sK + buf, Kh, kv_row, c0, T - 1, wave, lane);
-    async_tile_load<D, C::BN, C::NW>(sV + buf, Vh, kv_row, c0, T - 1, wave, lane);
+    copy.issue(sK + buf, sK_lds + 2 * buf, Kh, kv_row, c0, T - 1, wave, lane);
+    copy.issue(sV + buf, sV_lds + 2 * buf, Vh, kv_row, c0, T - 1, wave, lane);
   };
 
   f32x16 o[D / 32];
