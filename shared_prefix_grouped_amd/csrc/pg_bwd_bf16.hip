@@ -113,6 +113,10 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
     min_hi = min(min_hi, __shfl_xor(min_hi, w));
     max_hi = max(max_hi, __shfl_xor(max_hi, w));
   }
+  min_hi = __builtin_amdgcn_readfirstlane(min_hi);  // equal in every lane now
+  max_hi = __builtin_amdgcn_readfirstlane(max_hi);
+  SwzFrags<D> frag;
+  frag.init(lane);
 
   // K (role A) or V (role B) rows of the group as MFMA B operands:
   // column = key l32, k = d.
@@ -175,13 +179,13 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
 
   // Role A: S -> P for query block qb; P (fp32) goes to LDS for role B and,
   // packed to bf16, stays in registers for dV.
-  auto a_scores = [&](const bf16 *cQ, const float *cL, int c0, int qb, bf16x8 (&pk)[2]) {
+  auto a_scores = [&](lds_cchar *cQ, const float *cL, int c0, int qb, bf16x8 (&pk)[2]) {
     f32x16 s;
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = 0.f;
 #pragma unroll
     for (int st = 0; st < D / 16; ++st)
-      s = mfma32(lds_row_frag<D>(cQ, qb * 32 + l32, st * 16 + hi * 8), kvf[st], s);
+      s = mfma32(frag.row(cQ, qb * 32, st), kvf[st], s);
     const bool full = block_full(c0, qb);
 #pragma unroll
     for (int rq = 0; rq < 4; ++rq) {
@@ -204,23 +208,22 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
     pk[1] = pack8(s, 8);
   };
   // Role A: dV^T += dO^T P
-  auto a_dv = [&](const bf16 *cdO, int qb, const bf16x8 (&pk)[2]) {
+  auto a_dv = [&](lds_cchar *cdO, int qb, const bf16x8 (&pk)[2]) {
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
       for (int nb = 0; nb < D / 32; ++nb)
-        acc[nb] = mfma32(lds_tr_frag_swz<D>(cdO, qb * 32 + sub * 16, nb * 32, lane), pk[sub], acc[nb]);
+        acc[nb] = mfma32(frag.tr(cdO, qb * 32 + sub * 16, nb), pk[sub], acc[nb]);
   };
   // Role B: dP = dO V^T for query block qb
-  auto b_dp = [&](const bf16 *cdO, int qb, f32x16 &dp) {
+  auto b_dp = [&](lds_cchar *cdO, int qb, f32x16 &dp) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) dp[r] = 0.f;
 #pragma unroll
-    for (int st = 0; st < D / 16; ++st)
-      dp = mfma32(lds_row_frag<D>(cdO, qb * 32 + l32, st * 16 + hi * 8), kvf[st], dp);
+    for (int st = 0; st < D / 16; ++st) dp = mfma32(frag.row(cdO, qb * 32, st), kvf[st], dp);
   };
   // Role B: dS = P * (dP - delta), dK^T += Q^T dS
-  auto b_dk = [&](const bf16 *cQ, const float *cDl, int qb, f32x16 &dp) {
+  auto b_dk = [&](lds_cchar *cQ, const float *cDl, int qb, f32x16 &dp) {
 #pragma unroll
     for (int rq = 0; rq < 4; ++rq) {
       const int ql = qb * 32 + rq * 8 + hi * 4;
@@ -234,18 +237,18 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
       const bf16x8 db = pack8(dp, sub * 8);
 #pragma unroll
       for (int nb = 0; nb < D / 32; ++nb)
-        acc[nb] = mfma32(lds_tr_frag_swz<D>(cQ, qb * 32 + sub * 16, nb * 32, lane), db, acc[nb]);
+        acc[nb] = mfma32(frag.tr(cQ, qb * 32 + sub * 16, nb), db, acc[nb]);
     }
   };
 
   // Both roles run the same sequence of chunks and barriers (three per
   // chunk); the role is chosen once, outside the loop, so that each wave's
   // registers hold only its own role's state across the barriers.
-  auto chunk_buffers = [&](int ci, const bf16 *&cQ, const bf16 *&cdO, const float *&cL,
+  auto chunk_buffers = [&](int ci, lds_cchar *&cQ, lds_cchar *&cdO, const float *&cL,
                            const float *&cDl) {
     const int b = ci & 1;
-    cQ = sQ + b * C::BM * D;
-    cdO = sdO + b * C::BM * D;
+    cQ = lds_bytes(sQ + b * C::BM * D);
+    cdO = lds_bytes(sdO + b * C::BM * D);
     cL = sL + b * C::BM;
     cDl = sDl + b * C::BM;
   };
@@ -259,7 +262,7 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
       wait_async_loads();
       __syncthreads();
       if (ci + 1 < nC) issue(ci + 1);
-      const bf16 *cQ, *cdO;
+      lds_cchar *cQ, *cdO;
       const float *cL, *cDl;
       chunk_buffers(ci, cQ, cdO, cL, cDl);
       const bool live0 = block_live(c0, 0), live1 = block_live(c0, 1);
@@ -278,7 +281,7 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
       wait_async_loads();
       __syncthreads();
       if (ci + 1 < nC) issue(ci + 1);
-      const bf16 *cQ, *cdO;
+      lds_cchar *cQ, *cdO;
       const float *cL, *cDl;
       chunk_buffers(ci, cQ, cdO, cL, cDl);
       const bool live0 = block_live(c0, 0), live1 = block_live(c0, 1);
@@ -387,6 +390,8 @@ __global__ __launch_bounds__(256, 2) void dq_bf16_kernel(
   TileCopy<D, C::BN, C::NW> copy;
   copy.init(kv_row, wave, lane);
   const uint32_t sK_lds = lds_address(sK), sV_lds = lds_address(sV);
+  SwzFrags<D> frag;
+  frag.init(lane);
   auto issue = [&](int ci) {
     int c0, cend;
     chunk_range(ci, c0, cend);
@@ -408,8 +413,8 @@ __global__ __launch_bounds__(256, 2) void dq_bf16_kernel(
     wait_async_loads();
     __syncthreads();
     if (ci + 1 < nC) issue(ci + 1);
-    const bf16 *cK = sK + (ci & 1) * C::BN * D;
-    const bf16 *cV = sV + (ci & 1) * C::BN * D;
+    lds_cchar *cK = lds_bytes(sK + (ci & 1) * C::BN * D);
+    lds_cchar *cV = lds_bytes(sV + (ci & 1) * C::BN * D);
     if (!wave_active) continue;
     const int clast = min(c0 + C::BN, cend) - 1;
     if (c0 > qwl) continue;
@@ -427,8 +432,8 @@ __global__ __launch_bounds__(256, 2) void dq_bf16_kernel(
       }
 #pragma unroll
       for (int st = 0; st < D / 16; ++st) {
-        s = mfma32(lds_row_frag<D>(cK, b * 32 + l32, st * 16 + hi * 8), qf[st], s);
-        dp = mfma32(lds_row_frag<D>(cV, b * 32 + l32, st * 16 + hi * 8), of[st], dp);
+        s = mfma32(frag.row(cK, b * 32, st), qf[st], s);
+        dp = mfma32(frag.row(cV, b * 32, st), of[st], dp);
       }
       // register r holds key c0 + b*32 + mfma_row(r, hi); the lane's column is its query
 #pragma unroll
@@ -446,7 +451,7 @@ __global__ __launch_bounds__(256, 2) void dq_bf16_kernel(
         const bf16x8 db = pack8(s, sub * 8);
 #pragma unroll
         for (int nb = 0; nb < D / 32; ++nb)
-          dq[nb] = mfma32(lds_tr_frag_swz<D>(cK, b * 32 + sub * 16, nb * 32, lane), db, dq[nb]);
+          dq[nb] = mfma32(frag.tr(cK, b * 32 + sub * 16, nb), db, dq[nb]);
       }
     }
   }

@@ -254,6 +254,47 @@ __device__ __forceinline__ uint32_t lds_address(const void *p) {
 // decisions compile to scalar branches).
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
+typedef __attribute__((address_space(3))) const char lds_cchar;
+typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
+
+// MFMA operand fragments from a swizzled tile with the lane-dependent part of
+// the address computed once.  swz_chunk depends only on row % 16, so moving a
+// fragment by a multiple of 16 rows only adds row * D * 2 bytes, which the
+// compiler folds into the LDS instruction's immediate offset.
+template <int D>
+struct SwzFrags {
+  uint32_t row_off[D / 16];     // row l32, columns 16 st + 8 hi .. + 8
+  uint32_t tr_off[D / 32][2];   // transposing reads: see lds_tr_frag_swz
+
+  __device__ __forceinline__ void init(int lane) {
+    const int l32 = lane & 31, hi = lane >> 5, s = lane & 15;
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) row_off[st] = 2 * swz<D>(l32, st * 16 + hi * 8);
+#pragma unroll
+    for (int nb = 0; nb < D / 32; ++nb) {
+      const int col = nb * 32 + 16 * ((lane >> 4) & 1) + 4 * (s & 3);
+      const int row = 4 * hi + (s >> 2);
+      tr_off[nb][0] = 2 * swz<D>(row, col);
+      tr_off[nb][1] = 2 * swz<D>(row + 8, col);
+    }
+  }
+  // rows r0 + l32 (r0 a multiple of 16), 8 columns at 16 st + 8 hi
+  __device__ __forceinline__ bf16x8 row(lds_cchar *tile, int r0, int st) const {
+    return *reinterpret_cast<lds_bf16x8 *>(tile + row_off[st] + r0 * D * 2);
+  }
+  // lds_tr_frag_swz(tile, kb, 32 nb, lane), kb a multiple of 16
+  __device__ __forceinline__ bf16x8 tr(lds_cchar *tile, int kb, int nb) const {
+    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (lds_bf16x4 *)(tile + tr_off[nb][0] + kb * D * 2));
+    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (lds_bf16x4 *)(tile + tr_off[nb][1] + kb * D * 2));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+};
+
+// An LDS array as an address-space-3 byte pointer.
+__device__ __forceinline__ lds_cchar *lds_bytes(const void *p) { return (lds_cchar *)p; }
+
 __device__ __forceinline__ float wave_swap_halves(float x) { return __shfl_xor(x, 32); }
 
 // Pack 8 floats (registers r0..r0+7 of a 32x32 result) into bf16x8.

@@ -107,6 +107,8 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   TileCopy<D, C::BN, C::NW> copy;
   copy.init(kv_row, wave, lane);
   const uint32_t sK_lds = lds_address(sK), sV_lds = lds_address(sV);
+  SwzFrags<D> frag;
+  frag.init(lane);
   auto issue = [&](int ci) {
     int c0, cend;
     chunk_range(ci, c0, cend);
@@ -133,8 +135,8 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
     wait_async_loads();
     __syncthreads();
     if (ci + 1 < nC) issue(ci + 1);
-    const bf16 *cK = sK + (ci & 1) * C::BN * D;
-    const bf16 *cV = sV + (ci & 1) * C::BN * D;
+    lds_cchar *cK = lds_bytes(sK + (ci & 1) * C::BN * D);
+    lds_cchar *cV = lds_bytes(sV + (ci & 1) * C::BN * D);
     if (!wave_active) continue;
     const int clast = min(c0 + C::BN, cend) - 1;
     if (c0 > qwl) continue;                       // every key follows every row
@@ -150,7 +152,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
       for (int r = 0; r < 16; ++r) s[b][r] = 0.f;
 #pragma unroll
       for (int st = 0; st < D / 16; ++st) {
-        s[b] = mfma32(lds_row_frag<D>(cK, b * 32 + l32, st * 16 + hi * 8), qf[st], s[b]);
+        s[b] = mfma32(frag.row(cK, b * 32, st), qf[st], s[b]);
       }
     }
     if (!full) {
@@ -198,7 +200,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
         const bf16x8 pf = pack8(s[b], sub * 8);
 #pragma unroll
         for (int nb = 0; nb < D / 32; ++nb) {
-          const bf16x8 a = lds_tr_frag_swz<D>(cV, b * 32 + sub * 16, nb * 32, lane);
+          const bf16x8 a = frag.tr(cV, b * 32 + sub * 16, nb);
           o[nb] = mfma32(a, pf, o[nb]);
         }
       }
