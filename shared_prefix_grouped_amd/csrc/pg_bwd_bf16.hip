@@ -60,14 +60,25 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const Tin *__restrict__ O,
 // dK^T += Q^T dS, receiving P (fp32) from wave A through LDS.  Each wave then
 // holds one accumulator set and one K or V operand set, so two waves fit on
 // a SIMD and one's softmax arithmetic overlaps the other's matrix work.
+//
+// The query rows are walked in steps of 32 (one MFMA block), software-
+// pipelined by one step so that a single barrier per step suffices: in step n
+// wave A forms P_n and then adds block n-1 into dV; wave B forms dS_{n-1}
+// (P_{n-1} was published by the barrier that opened step n), adds it into
+// dK, and then computes dP_n, which it keeps in registers for the next step.
+// Q/dO rows (+ LSE and delta) live in a ring of NSLOT LDS slots, copied two
+// steps ahead: step n reads slots n and n-1.
 template <int D>
 struct DkdvCfg {
   static constexpr int BN = PG_TILE_KV;  // key rows per workgroup
   static constexpr int NG = BN / 32;     // 32-key groups
   static constexpr int NW = 2 * NG;      // waves: role A and role B per key group
   static constexpr int NT = NW * 64;
-  static constexpr int BM = 64;          // query rows per chunk
-  static constexpr int NQB = BM / 32;    // 32-row query blocks per chunk
+  static constexpr int BM = 32;          // query rows per step
+  static constexpr int NSLOT = 4;        // ring slots: n-1, n in use, n+1, n+2 in flight
+  static constexpr int NI = BM * D / 512;             // 1-KB copy instructions per tensor
+  static constexpr int NCW = NI < NW ? NI : NW;       // waves that copy one tensor
+  static constexpr bool SPLIT = 2 * NCW <= NW;        // Q and dO copied by disjoint waves
 };
 
 template <int D>
@@ -78,16 +89,15 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
     bf16 *__restrict__ dK, bf16 *__restrict__ dV, int T, int Hq, int Hkv, float scale_log2,
     float scale) {
   using C = DkdvCfg<D>;
-  static_assert(C::NQB == 2, "the P hand-off below is double-buffered by query block parity");
-  // Q and dO chunks (+ their base-2 LSE and delta), double-buffered, row-major
-  // and swizzled: read as MFMA rows for S = Q K^T and dP = dO V^T, and
-  // transposed for dV^T += dO^T P and dK^T += Q^T dS.
-  __shared__ __attribute__((aligned(16))) bf16 sQ[2 * C::BM * D];
-  __shared__ __attribute__((aligned(16))) bf16 sdO[2 * C::BM * D];
-  __shared__ __attribute__((aligned(16))) float sL[2 * C::BM];
-  __shared__ __attribute__((aligned(16))) float sDl[2 * C::BM];
-  // P of one 32x32 block per key group, by query-block parity, in the
-  // accumulator layout: [group][parity][register quad][lane].
+  // Q and dO rows of a step, row-major and swizzled: read as MFMA rows for
+  // S = Q K^T and dP = dO V^T, and transposed for dV^T += dO^T P and
+  // dK^T += Q^T dS.  LSE / delta slots hold 64 floats (32 used).
+  __shared__ __attribute__((aligned(16))) bf16 sQ[C::NSLOT * C::BM * D];
+  __shared__ __attribute__((aligned(16))) bf16 sdO[C::NSLOT * C::BM * D];
+  __shared__ __attribute__((aligned(16))) float sL[C::NSLOT * 64];
+  __shared__ __attribute__((aligned(16))) float sDl[C::NSLOT * 64];
+  // P of one 32x32 block per key group, by step parity, in the accumulator
+  // layout: [group][parity][register quad][lane].
   __shared__ __attribute__((aligned(16))) f32x4 sP[C::NG][2][4][64];
 
   int tile, hk;
@@ -133,6 +143,10 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
       }
     }
   }
+  // Let these loads complete here: left to the compiler, the wait for them
+  // lands at their first use inside the step loop, where it would also wait
+  // for the prefetch copies issued in the same step.
+  wait_async_loads();
 
   // dV^T (role A) or dK^T (role B): register r of lane l holds
   // d = 32 nb + mfma_row(r, hi), key = l32.
@@ -142,156 +156,152 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[nb][r] = 0.f;
 
-  const int nQ = (qend - k0 + C::BM - 1) / C::BM;  // chunks per query head
-  const int nC = nQ * rep;
+  // Steps: 32-row query blocks [k0 + 32 b, ...) for b = nB-1 down to 0, the
+  // query heads of the kv head interleaved per block.  Walking down from
+  // the end of the group, which every prefix tile of the group shares, keeps
+  // the workgroups that run side by side on one XCD on the same Q/dO rows,
+  // so those rows are fetched into that XCD's L2 once.
+  const int nB = (qend - k0 + C::BM - 1) / C::BM;  // blocks per query head
+  const int nS = nB * rep;
   const size_t q_row = (size_t)Hq * D;
-  auto chunk_of = [&](int ci, int &h, int &c0) {
-    const int hh = ci / nQ;
-    h = hk * rep + hh;
-    c0 = k0 + (ci - hh * nQ) * C::BM;
+  auto step_of = [&](int n, int &h, int &c0) {
+    const int bi = n / rep;
+    h = hk * rep + (n - bi * rep);
+    c0 = k0 + (nB - 1 - bi) * C::BM;
   };
-  // chunk ci lives in LDS buffer ci % 2 and is copied one chunk ahead
-  TileCopy<D, C::BM, C::NW> copy;
-  copy.init(q_row, wave, lane);
+
+  // Copies of step n into slot n % NSLOT: Q and dO by NCW waves each (the
+  // same waves, or disjoint ones when a tensor needs fewer instructions than
+  // there are waves), LSE by wave 0 and delta by wave 1.
+  using Copy = TileCopy<D, C::BM, C::NCW>;
+  const bool copy_q = wave < C::NCW;
+  const bool copy_do = C::SPLIT ? (wave >= C::NCW && wave < 2 * C::NCW) : copy_q;
+  const int cw_do = C::SPLIT ? wave - C::NCW : wave;
+  Copy cq, cdo;
+  cq.init(q_row, wave, lane);
+  cdo.init(q_row, cw_do, lane);
+  const int dma_per_step = (copy_q ? Copy::PER_WAVE : 0) + (copy_do ? Copy::PER_WAVE : 0) +
+                           (wave == 0) + (wave == 1);
   const uint32_t sQ_lds = lds_address(sQ), sdO_lds = lds_address(sdO);
-  auto issue = [&](int ci) {
+  auto issue = [&](int n) {
     int h, c0;
-    chunk_of(ci, h, c0);
-    const int b = ci & 1;
-    const int buf = b * C::BM * D;
-    copy.issue(sQ + buf, sQ_lds + 2 * buf, Q + (size_t)h * D, q_row, c0, T - 1, wave, lane);
-    copy.issue(sdO + buf, sdO_lds + 2 * buf, dO + (size_t)h * D, q_row, c0, T - 1, wave, lane);
-    if (wave == 0) async_row_load64(sL + b * C::BM, LSE2 + (size_t)h * T + c0, T - 1 - c0, lane);
-    if (wave == 1) async_row_load64(sDl + b * C::BM, Delta + (size_t)h * T + c0, T - 1 - c0, lane);
+    step_of(n, h, c0);
+    const int slot = n % C::NSLOT;
+    const int buf = slot * C::BM * D;
+    if (copy_q) cq.issue(sQ + buf, sQ_lds + 2 * buf, Q + (size_t)h * D, q_row, c0, T - 1, wave, lane);
+    if (copy_do)
+      cdo.issue(sdO + buf, sdO_lds + 2 * buf, dO + (size_t)h * D, q_row, c0, T - 1, cw_do, lane);
+    if (wave == 0) async_row_load64(sL + slot * 64, LSE2 + (size_t)h * T + c0, T - 1 - c0, lane);
+    if (wave == 1) async_row_load64(sDl + slot * 64, Delta + (size_t)h * T + c0, T - 1 - c0, lane);
   };
-  static_assert(C::BM == 64, "LSE/delta rows are copied by one wave instruction each");
+  // Start of step n: slot n has landed for every wave (the copies of slot
+  // n+1 may still be in flight), and every wave has finished step n-1.
+  // The copies for step n+2 go into the slot that step n-1 read last.
+  auto open_step = [&](int n) {
+    if (n < nS) wait_async_loads_leaving(n + 1 < nS ? dma_per_step : 0);
+    __syncthreads();
+    if (n + 2 < nS) issue(n + 2);
+  };
+  auto slot_q = [&](int n) { return lds_bytes(sQ + (n % C::NSLOT) * C::BM * D); };
+  auto slot_do = [&](int n) { return lds_bytes(sdO + (n % C::NSLOT) * C::BM * D); };
 
-  // Whether query block qb of chunk c0 meets the group's keys at all, and
+  // Whether query block [c0, c0 + 32) meets the group's keys at all, and
   // whether every (query, key) pair of it is visible.
-  auto block_live = [&](int c0, int qb) {
-    const int cq = c0 + qb * 32;
-    return group_active && !(cq + 31 < kw0 || cq >= max_hi);
-  };
-  auto block_full = [&](int c0, int qb) {
-    const int cq = c0 + qb * 32;
-    return (cq >= kwl) && (cq + 32 <= min_hi);
-  };
+  auto block_live = [&](int c0) { return group_active && !(c0 + 31 < kw0 || c0 >= max_hi); };
+  auto block_full = [&](int c0) { return (c0 >= kwl) && (c0 + 32 <= min_hi); };
 
-  // Role A: S -> P for query block qb; P (fp32) goes to LDS for role B and,
-  // packed to bf16, stays in registers for dV.
-  auto a_scores = [&](lds_cchar *cQ, const float *cL, int c0, int qb, bf16x8 (&pk)[2]) {
-    f32x16 s;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s[r] = 0.f;
-#pragma unroll
-    for (int st = 0; st < D / 16; ++st)
-      s = mfma32(frag.row(cQ, qb * 32, st), kvf[st], s);
-    const bool full = block_full(c0, qb);
-#pragma unroll
-    for (int rq = 0; rq < 4; ++rq) {
-      const int ql = qb * 32 + rq * 8 + hi * 4;
-      const f32x4 Lq = *reinterpret_cast<const f32x4 *>(&cL[ql]);
-      f32x4 pq;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float p = fast_exp2(fmaf(s[rq * 4 + j], scale_log2, -Lq[j]));
-        if (!full) {
-          const int qr = c0 + ql + j;
-          p = (key <= qr && qr < hik) ? p : 0.f;
-        }
-        s[rq * 4 + j] = p;
-        pq[j] = p;
-      }
-      sP[kg][qb & 1][rq][lane] = pq;
-    }
-    pk[0] = pack8(s, 0);
-    pk[1] = pack8(s, 8);
-  };
-  // Role A: dV^T += dO^T P
-  auto a_dv = [&](lds_cchar *cdO, int qb, const bf16x8 (&pk)[2]) {
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-      for (int nb = 0; nb < D / 32; ++nb)
-        acc[nb] = mfma32(frag.tr(cdO, qb * 32 + sub * 16, nb), pk[sub], acc[nb]);
-  };
-  // Role B: dP = dO V^T for query block qb
-  auto b_dp = [&](lds_cchar *cdO, int qb, f32x16 &dp) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) dp[r] = 0.f;
-#pragma unroll
-    for (int st = 0; st < D / 16; ++st) dp = mfma32(frag.row(cdO, qb * 32, st), kvf[st], dp);
-  };
-  // Role B: dS = P * (dP - delta), dK^T += Q^T dS
-  auto b_dk = [&](lds_cchar *cQ, const float *cDl, int qb, f32x16 &dp) {
-#pragma unroll
-    for (int rq = 0; rq < 4; ++rq) {
-      const int ql = qb * 32 + rq * 8 + hi * 4;
-      const f32x4 Dq = *reinterpret_cast<const f32x4 *>(&cDl[ql]);
-      const f32x4 pq = sP[kg][qb & 1][rq][lane];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) dp[rq * 4 + j] = pq[j] * (dp[rq * 4 + j] - Dq[j]);
-    }
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      const bf16x8 db = pack8(dp, sub * 8);
-#pragma unroll
-      for (int nb = 0; nb < D / 32; ++nb)
-        acc[nb] = mfma32(frag.tr(cQ, qb * 32 + sub * 16, nb), db, acc[nb]);
-    }
-  };
-
-  // Both roles run the same sequence of chunks and barriers (three per
-  // chunk); the role is chosen once, outside the loop, so that each wave's
-  // registers hold only its own role's state across the barriers.
-  auto chunk_buffers = [&](int ci, lds_cchar *&cQ, lds_cchar *&cdO, const float *&cL,
-                           const float *&cDl) {
-    const int b = ci & 1;
-    cQ = lds_bytes(sQ + b * C::BM * D);
-    cdO = lds_bytes(sdO + b * C::BM * D);
-    cL = sL + b * C::BM;
-    cDl = sDl + b * C::BM;
-  };
-  if (nC > 0) issue(0);
+  if (nS > 0) issue(0);
+  if (nS > 1) issue(1);
   if (roleA) {
-    for (int ci = 0; ci < nC; ++ci) {
-      int h, c0;
-      chunk_of(ci, h, c0);
-      // chunk ci has landed for every wave, and every wave is done reading
-      // the other buffer, which the next copy overwrites
-      wait_async_loads();
-      __syncthreads();
-      if (ci + 1 < nC) issue(ci + 1);
-      lds_cchar *cQ, *cdO;
-      const float *cL, *cDl;
-      chunk_buffers(ci, cQ, cdO, cL, cDl);
-      const bool live0 = block_live(c0, 0), live1 = block_live(c0, 1);
-      bf16x8 pk0[2], pk1[2];
-      if (live0) a_scores(cQ, cL, c0, 0, pk0);
-      __syncthreads();  // P of block 0 is in LDS
-      if (live0) a_dv(cdO, 0, pk0);
-      if (live1) a_scores(cQ, cL, c0, 1, pk1);
-      __syncthreads();  // P of block 1 is in LDS
-      if (live1) a_dv(cdO, 1, pk1);
+    // S -> P for step n; P (fp32) goes to LDS for wave B and, packed to
+    // bf16, stays in registers for dV in the next step.
+    bf16x8 pk[2];
+    bool live_prev = false;
+    for (int n = 0; n <= nS; ++n) {
+      open_step(n);
+      int h = 0, c0 = 0;
+      if (n < nS) step_of(n, h, c0);
+      const bool live = n < nS && block_live(c0);
+      bf16x8 pn[2];
+      if (live) {
+        lds_cchar *cQ = slot_q(n);
+        const float *cL = sL + (n % C::NSLOT) * 64;
+        f32x16 s;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[r] = 0.f;
+#pragma unroll
+        for (int st = 0; st < D / 16; ++st) s = mfma32(frag.row(cQ, 0, st), kvf[st], s);
+        const bool full = block_full(c0);
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          const int ql = rq * 8 + hi * 4;
+          const f32x4 Lq = *reinterpret_cast<const f32x4 *>(&cL[ql]);
+          f32x4 pq;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            float p = fast_exp2(fmaf(s[rq * 4 + j], scale_log2, -Lq[j]));
+            if (!full) {
+              const int qr = c0 + ql + j;
+              p = (key <= qr && qr < hik) ? p : 0.f;
+            }
+            s[rq * 4 + j] = p;
+            pq[j] = p;
+          }
+          sP[kg][n & 1][rq][lane] = pq;
+        }
+        pn[0] = pack8(s, 0);
+        pn[1] = pack8(s, 8);
+      }
+      if (live_prev) {
+        // dV^T += dO_{n-1}^T P_{n-1}
+        lds_cchar *cdO = slot_do(n - 1);
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+          for (int nb = 0; nb < D / 32; ++nb)
+            acc[nb] = mfma32(frag.tr(cdO, sub * 16, nb), pk[sub], acc[nb]);
+      }
+      pk[0] = pn[0];
+      pk[1] = pn[1];
+      live_prev = live;
     }
   } else {
-    for (int ci = 0; ci < nC; ++ci) {
-      int h, c0;
-      chunk_of(ci, h, c0);
-      wait_async_loads();
-      __syncthreads();
-      if (ci + 1 < nC) issue(ci + 1);
-      lds_cchar *cQ, *cdO;
-      const float *cL, *cDl;
-      chunk_buffers(ci, cQ, cdO, cL, cDl);
-      const bool live0 = block_live(c0, 0), live1 = block_live(c0, 1);
-      f32x16 dp0, dp1;
-      if (live0) b_dp(cdO, 0, dp0);
-      __syncthreads();  // P of block 0 is in LDS
-      if (live0) b_dk(cQ, cDl, 0, dp0);
-      if (live1) b_dp(cdO, 1, dp1);
-      __syncthreads();  // P of block 1 is in LDS
-      if (live1) b_dk(cQ, cDl, 1, dp1);
+    f32x16 dp;  // dP of the previous step
+    bool live_prev = false;
+    for (int n = 0; n <= nS; ++n) {
+      open_step(n);
+      int h = 0, c0 = 0;
+      if (n < nS) step_of(n, h, c0);
+      const bool live = n < nS && block_live(c0);
+      if (live_prev) {
+        // dS_{n-1} = P_{n-1} * (dP_{n-1} - delta), dK^T += Q_{n-1}^T dS_{n-1}
+        lds_cchar *cQ = slot_q(n - 1);
+        const float *cDl = sDl + ((n - 1) % C::NSLOT) * 64;
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          const int ql = rq * 8 + hi * 4;
+          const f32x4 Dq = *reinterpret_cast<const f32x4 *>(&cDl[ql]);
+          const f32x4 pq = sP[kg][(n - 1) & 1][rq][lane];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) dp[rq * 4 + j] = pq[j] * (dp[rq * 4 + j] - Dq[j]);
+        }
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) {
+          const bf16x8 db = pack8(dp, sub * 8);
+#pragma unroll
+          for (int nb = 0; nb < D / 32; ++nb)
+            acc[nb] = mfma32(frag.tr(cQ, sub * 16, nb), db, acc[nb]);
+        }
+      }
+      if (live) {
+        // dP_n = dO_n V^T
+        lds_cchar *cdO = slot_do(n);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dp[r] = 0.f;
+#pragma unroll
+        for (int st = 0; st < D / 16; ++st) dp = mfma32(frag.row(cdO, 0, st), kvf[st], dp);
+      }
+      live_prev = live;
     }
   }
 

@@ -211,6 +211,20 @@ __device__ __forceinline__ void async_row_load64(float *dst, const float *src, i
 // loads, including the direct-to-LDS ones, have completed.
 __device__ __forceinline__ void wait_async_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// s_waitcnt vmcnt(n) for a wave-uniform n in [0, 3]: all but this wave's n
+// most recently issued global loads have completed (loads complete in order).
+__device__ __forceinline__ void wait_async_loads_leaving(int n) {
+  if (n >= 3) {
+    __builtin_amdgcn_s_waitcnt(0x0F73);
+  } else if (n == 2) {
+    __builtin_amdgcn_s_waitcnt(0x0F72);
+  } else if (n == 1) {
+    __builtin_amdgcn_s_waitcnt(0x0F71);
+  } else {
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+  }
+}
+
 // Work item of a block in a grid of n_tiles x Hq blocks, one per (tile, query
 // head).  Workgroups are dispatched to the 8 XCDs round-robin by block index
 // and each XCD has its own L2; when the kv heads split evenly over the XCDs,
