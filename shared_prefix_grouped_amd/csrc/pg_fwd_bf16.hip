@@ -102,7 +102,6 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
       cend = b1;
     }
   };
-  // chunk ci goes to LDS buffer ci % 2, copied asynchronously one chunk ahead
   // chunk ci lives in LDS buffer ci % 2 and is copied one chunk ahead
   TileCopy<D, C::BN, C::NW> copy;
   copy.init(kv_row, wave, lane);
