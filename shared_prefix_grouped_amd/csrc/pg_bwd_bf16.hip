@@ -61,13 +61,12 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const Tin *__restrict__ O,
 // holds one accumulator set and one K or V operand set, so two waves fit on
 // a SIMD and one's softmax arithmetic overlaps the other's matrix work.
 //
-// The query rows are walked in steps of 32 (one MFMA block), software-
-// pipelined by one step so that a single barrier per step suffices: in step n
-// wave A forms P_n and then adds block n-1 into dV; wave B forms dS_{n-1}
-// (P_{n-1} was published by the barrier that opened step n), adds it into
-// dK, and then computes dP_n, which it keeps in registers for the next step.
-// Q/dO rows (+ LSE and delta) live in a ring of NSLOT LDS slots, copied two
-// steps ahead: step n reads slots n and n-1.
+// The query rows are walked in steps of 32 (one MFMA block) with one barrier
+// per step: in step n wave A forms P_n, publishes it in LDS and adds block n
+// into dV; wave B forms dS_{n-1} (P_{n-1} was published by the barrier that
+// opened step n), adds it into dK, and computes dP_n, which it keeps in
+// registers for the next step.  Q/dO rows (+ LSE, delta) live in a ring of
+// NSLOT LDS slots, staged through registers (see stage / commit below).
 template <int D>
 struct DkdvCfg {
   static constexpr int BN = PG_TILE_KV;  // key rows per workgroup
@@ -75,10 +74,7 @@ struct DkdvCfg {
   static constexpr int NW = 2 * NG;      // waves: role A and role B per key group
   static constexpr int NT = NW * 64;
   static constexpr int BM = 32;          // query rows per step
-  static constexpr int NSLOT = 4;        // ring slots: n-1, n in use, n+1, n+2 in flight
-  static constexpr int NI = BM * D / 512;             // 1-KB copy instructions per tensor
-  static constexpr int NCW = NI < NW ? NI : NW;       // waves that copy one tensor
-  static constexpr bool SPLIT = 2 * NCW <= NW;        // Q and dO copied by disjoint waves
+  static constexpr int NSLOT = 4;        // ring slots: n-1, n read; n+1 landed; n+2 being written
 };
 
 template <int D>
@@ -170,37 +166,55 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
     c0 = k0 + (nB - 1 - bi) * C::BM;
   };
 
-  // Copies of step n into slot n % NSLOT: Q and dO by NCW waves each (the
-  // same waves, or disjoint ones when a tensor needs fewer instructions than
-  // there are waves), LSE by wave 0 and delta by wave 1.
-  using Copy = TileCopy<D, C::BM, C::NCW>;
-  const bool copy_q = wave < C::NCW;
-  const bool copy_do = C::SPLIT ? (wave >= C::NCW && wave < 2 * C::NCW) : copy_q;
-  const int cw_do = C::SPLIT ? wave - C::NCW : wave;
-  Copy cq, cdo;
-  cq.init(q_row, wave, lane);
-  cdo.init(q_row, cw_do, lane);
-  const int dma_per_step = (copy_q ? Copy::PER_WAVE : 0) + (copy_do ? Copy::PER_WAVE : 0) +
-                           (wave == 0) + (wave == 1);
-  const uint32_t sQ_lds = lds_address(sQ), sdO_lds = lds_address(sdO);
-  auto issue = [&](int n) {
+  // Copies of step n into slot n % NSLOT go through registers: every thread
+  // loads one 16-byte chunk of Q and of dO (and waves 0 / 1 one LSE / delta
+  // value per row) at step n-3 and stores them into LDS with ordinary LDS
+  // writes at step n-2, after the barrier that retired the slot's previous
+  // rows.  (Direct global->LDS copies would compete with the fragment reads
+  // of both roles for the LDS, and lose: the step would wait for them.)
+  static_assert(C::BM * D / 8 == C::NT || C::BM * D / 8 == C::NT / 2,
+                "one or half a chunk of each tensor per thread and step");
+  constexpr int CPR = D / 8;                           // 16-byte chunks per row
+  const bool chunk_owner = tid < C::BM * CPR;
+  const int crow = tid / CPR, cch = tid % CPR;
+  const int cdst = crow * D + ((cch ^ swz_chunk<D>(crow)) << 3);  // swizzled, elements
+  // Buffer resources over Q, dO, LSE2 and delta: a load is then a scalar
+  // descriptor + a scalar per-step offset + the thread's fixed byte offset,
+  // so it holds no per-step vector address registers, and rows past the end
+  // of a tensor read as zero (the visibility mask covers them).
+  const __amdgpu_buffer_rsrc_t rQ = buffer_resource(Q, (size_t)T * q_row * sizeof(bf16));
+  const __amdgpu_buffer_rsrc_t rdO = buffer_resource(dO, (size_t)T * q_row * sizeof(bf16));
+  const __amdgpu_buffer_rsrc_t rL = buffer_resource(wave == 0 ? LSE2 : Delta, (size_t)Hq * T * 4);
+  const int coff = crow * (int)(q_row * sizeof(bf16)) + cch * 16;  // thread's chunk in a step
+  bf16x8 stq, sto;
+  float stl = 0.f;
+  auto stage = [&](int n) {
     int h, c0;
     step_of(n, h, c0);
-    const int slot = n % C::NSLOT;
-    const int buf = slot * C::BM * D;
-    if (copy_q) cq.issue(sQ + buf, sQ_lds + 2 * buf, Q + (size_t)h * D, q_row, c0, T - 1, wave, lane);
-    if (copy_do)
-      cdo.issue(sdO + buf, sdO_lds + 2 * buf, dO + (size_t)h * D, q_row, c0, T - 1, cw_do, lane);
-    if (wave == 0) async_row_load64(sL + slot * 64, LSE2 + (size_t)h * T + c0, T - 1 - c0, lane);
-    if (wave == 1) async_row_load64(sDl + slot * 64, Delta + (size_t)h * T + c0, T - 1 - c0, lane);
+    if (chunk_owner) {
+      const int soff = (int)(((size_t)c0 * q_row + (size_t)h * D) * sizeof(bf16));
+      stq = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rQ, coff, soff, 0));
+      sto = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rdO, coff, soff, 0));
+    }
+    if (wave < 2 && lane < C::BM)
+      stl = __builtin_bit_cast(
+          float, __builtin_amdgcn_raw_buffer_load_b32(rL, lane * 4, (int)(((size_t)h * T + c0) * 4), 0));
   };
-  // Start of step n: slot n has landed for every wave (the copies of slot
-  // n+1 may still be in flight), and every wave has finished step n-1.
-  // The copies for step n+2 go into the slot that step n-1 read last.
+  auto commit = [&](int n) {
+    const int slot = n % C::NSLOT;
+    if (chunk_owner) {
+      *reinterpret_cast<bf16x8 *>(sQ + slot * C::BM * D + cdst) = stq;
+      *reinterpret_cast<bf16x8 *>(sdO + slot * C::BM * D + cdst) = sto;
+    }
+    if (wave < 2 && lane < C::BM) (wave == 0 ? sL : sDl)[slot * 64 + lane] = stl;
+  };
+  // Start of step n: every wave has finished step n-1 and slot n (written
+  // in step n-2) is visible.  Then slot n+2, last read in step n-1, receives
+  // the rows staged in step n-1, and the rows of step n+3 are loaded.
   auto open_step = [&](int n) {
-    if (n < nS) wait_async_loads_leaving(n + 1 < nS ? dma_per_step : 0);
     __syncthreads();
-    if (n + 2 < nS) issue(n + 2);
+    if (n + 2 < nS) commit(n + 2);
+    if (n + 3 < nS) stage(n + 3);
   };
   auto slot_q = [&](int n) { return lds_bytes(sQ + (n % C::NSLOT) * C::BM * D); };
   auto slot_do = [&](int n) { return lds_bytes(sdO + (n % C::NSLOT) * C::BM * D); };
@@ -210,20 +224,22 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
   auto block_live = [&](int c0) { return group_active && !(c0 + 31 < kw0 || c0 >= max_hi); };
   auto block_full = [&](int c0) { return (c0 >= kwl) && (c0 + 32 <= min_hi); };
 
-  if (nS > 0) issue(0);
-  if (nS > 1) issue(1);
+  for (int j = 0; j < 3 && j < nS; ++j) {
+    stage(j);
+    if (j < 2) commit(j);
+  }
+  // Drain the prologue's loads here: otherwise the compiler's wait analysis
+  // carries them into the loop and waits for every step's own loads mid-step.
+  wait_async_loads();
   if (roleA) {
-    // S -> P for step n; P (fp32) goes to LDS for wave B and, packed to
-    // bf16, stays in registers for dV in the next step.
-    bf16x8 pk[2];
-    bool live_prev = false;
+    // S -> P for step n; P (fp32) goes to LDS for wave B (which uses it in
+    // step n+1) and, packed to bf16, into dV^T += dO_n^T P_n right away.
+    // The loop runs to n = nS so that every wave meets the same barriers.
     for (int n = 0; n <= nS; ++n) {
       open_step(n);
       int h = 0, c0 = 0;
       if (n < nS) step_of(n, h, c0);
-      const bool live = n < nS && block_live(c0);
-      bf16x8 pn[2];
-      if (live) {
+      if (n < nS && block_live(c0)) {
         lds_cchar *cQ = slot_q(n);
         const float *cL = sL + (n % C::NSLOT) * 64;
         f32x16 s;
@@ -249,21 +265,13 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
           }
           sP[kg][n & 1][rq][lane] = pq;
         }
-        pn[0] = pack8(s, 0);
-        pn[1] = pack8(s, 8);
-      }
-      if (live_prev) {
-        // dV^T += dO_{n-1}^T P_{n-1}
-        lds_cchar *cdO = slot_do(n - 1);
+        const bf16x8 p0 = pack8(s, 0), p1 = pack8(s, 8);
+        lds_cchar *cdO = slot_do(n);
 #pragma unroll
-        for (int sub = 0; sub < 2; ++sub)
+        for (int nb = 0; nb < D / 32; ++nb) acc[nb] = mfma32(frag.tr(cdO, 0, nb), p0, acc[nb]);
 #pragma unroll
-          for (int nb = 0; nb < D / 32; ++nb)
-            acc[nb] = mfma32(frag.tr(cdO, sub * 16, nb), pk[sub], acc[nb]);
+        for (int nb = 0; nb < D / 32; ++nb) acc[nb] = mfma32(frag.tr(cdO, 16, nb), p1, acc[nb]);
       }
-      pk[0] = pn[0];
-      pk[1] = pn[1];
-      live_prev = live;
     }
   } else {
     f32x16 dp;  // dP of the previous step

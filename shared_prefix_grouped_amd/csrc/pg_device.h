@@ -259,6 +259,26 @@ __device__ __forceinline__ void xcd_kvhead_work(int bid, int Hkv, int &tile, int
   }
 }
 
+// Raw buffer resource (stride 0) over `bytes` bytes at `p`, for buffer loads
+// with a scalar descriptor: accesses at or past `bytes` return zero.  Word 3
+// is the gfx9-family raw-buffer format (32-bit data, no swizzle).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_resource(const void *p, size_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+typedef __attribute__((address_space(1))) const char gbl_cchar;
+typedef __attribute__((address_space(1))) const bf16x8 gbl_bf16x8;
+
+// A wave-uniform global pointer, as a global-address-space byte pointer held
+// in scalar registers (so that `uniform_ptr(p) + lane_offset` compiles to the
+// scalar-base form of a global load).
+__device__ __forceinline__ gbl_cchar *uniform_ptr(const void *p) {
+  const uint64_t a = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return (gbl_cchar *)(((uint64_t)hi << 32) | lo);
+}
+
 // Byte address of an LDS array in the LDS aperture (for M0), as a scalar.
 __device__ __forceinline__ uint32_t lds_address(const void *p) {
   return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_char *)p);
