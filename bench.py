@@ -1,11 +1,16 @@
 """Benchmark of grouped shared-prefix attention (fwd + bwd) on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--no-baseline] [--no-cpu] [--cpu-seconds S]
+                    [--no-baseline] [--no-cpu] [--cpu-seconds S] [--forward-only]
 
 One step is one pass of the whole path over one packed batch with inputs
 already resident in HBM: pg_pack (plan + descriptor upload), pg_attn_fwd and
 pg_attn_bwd.  Prints ONE JSON line on stdout; progress goes to stderr.
+
+--forward-only  scoring mode: a step is pg_pack + pg_attn_fwd without the
+           logsumexp store (many short responses scored against one long
+           context; default workload bf16_scoring_p32768); value is then
+           4 * d * Hq * pairs / step time.
 
 value      effective TFLOP/s = 14 * d * Hq * pairs / step time, where pairs is
            the number of unmasked (query, key) pairs per head of the grouped
@@ -38,6 +43,7 @@ PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 METRIC = "grouped-attn fwd+bwd TFLOP/s & % MFMA peak; speedup vs repeated-prefix"
+METRIC_FWD = "grouped-attn forward-only scoring TFLOP/s & % MFMA peak; speedup vs repeated-prefix"
 
 # algorithmic flops per unmasked (query, key) pair and query head, per kernel
 KERNEL_FLOPS_PER_PAIR_D = {"fwd": 4, "bwd_dkdv": 8, "bwd_dq": 6}
@@ -52,7 +58,10 @@ def parse(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="bf16_gqa_g16_p8192")
+    ap.add_argument("--workload", default=None,
+                    help="bf16_gqa_g16_p8192 (default), or bf16_scoring_p32768 with --forward-only")
+    ap.add_argument("--forward-only", action="store_true",
+                    help="score without backward and without storing the logsumexp")
     ap.add_argument("--no-baseline", action="store_true", help="skip the repeated-prefix run")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -101,8 +110,9 @@ def groups_of(w):
 class Runner:
     """Holds device inputs/outputs for one layout and runs steps through the C ABI."""
 
-    def __init__(self, pg, torch, groups, w, tensors):
+    def __init__(self, pg, torch, groups, w, tensors, forward_only=False):
         self.pg, self.torch, self.groups, self.w = pg, torch, groups, w
+        self.forward_only = forward_only
         self.q, self.k, self.v, self.do = tensors
         self.batch = pg.pg_pack(groups, w.num_q_heads, w.num_kv_heads, w.head_dim)
         T = self.batch.total_rows
@@ -120,6 +130,9 @@ class Runner:
         pg = self.pg
         w = self.w
         self.batch = pg.pg_pack(self.groups, w.num_q_heads, w.num_kv_heads, w.head_dim)
+        if self.forward_only:
+            pg.pg_attn_fwd(self.batch, self.q, self.k, self.v, None, out=self.o, store_lse=False)
+            return
         pg.pg_attn_fwd(self.batch, self.q, self.k, self.v, None, out=self.o, lse=self.lse)
         pg.pg_attn_bwd(self.batch, self.q, self.k, self.v, self.o, self.lse, self.do, None,
                        dq=self.dq, dk=self.dk, dv=self.dv, workspace=self.ws)
@@ -144,7 +157,7 @@ class Runner:
         return start.elapsed_time(stop) / steps, wall / steps, kernels
 
 
-def cpu_baseline(w, arrs, budget_s):
+def cpu_baseline(w, arrs, budget_s, forward_only=False):
     """The oracle as it stands, on kv head 0 and the first members of group 0."""
     from oracle.attention import pair_counts, repeated_prefix_attention
     try:
@@ -161,20 +174,23 @@ def cpu_baseline(w, arrs, budget_s):
         rows = np.concatenate([np.arange(P), np.arange(s, s + r)])
         sub = {k: v[rows] for k, v in arrs.items()}
         t0 = time.perf_counter()
-        repeated_prefix_attention([(P, [r])], sub["q"], sub["k"], sub["v"], sub["do"], kv_heads=[0])
+        repeated_prefix_attention([(P, [r])], sub["q"], sub["k"], sub["v"],
+                                  None if forward_only else sub["do"], kv_heads=[0])
         elapsed += time.perf_counter() - t0
         done.append(r)
         log(f"[bench] cpu oracle: member {i} (P={P}, R={r}) done, {elapsed:.1f}s")
         if elapsed >= budget_s:
             break
     pairs, _ = pair_counts([(P, done)])
-    flops = 14.0 * w.head_dim * rep * pairs
+    per_pair = 4.0 if forward_only else 14.0
+    flops = per_pair * w.head_dim * rep * pairs
     return {
         "value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(threads),
         "kind": "oracle",
         "sample": (f"fp64 repeated-prefix oracle, kv head 0 ({rep} query heads), group 0 prefix "
-                   f"P={P} with its first {len(done)} responses {done}; {elapsed:.1f} s; credited "
-                   f"14*d*heads*pairs of that grouped sub-batch ({pairs} pairs)"),
+                   f"P={P} with its first {len(done)} responses {done}{' (forward only)' if forward_only else ''}; "
+                   f"{elapsed:.1f} s; credited {int(per_pair)}*d*heads*pairs of that grouped sub-batch "
+                   f"({pairs} pairs)"),
         "seconds": elapsed,
     }
 
@@ -193,7 +209,8 @@ def main(argv=None) -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
     pg.lib()  # fails loudly when the HIP library is not built
-    w = attention_workloads()[a.workload]
+    fwd_only = a.forward_only
+    w = attention_workloads()[a.workload or ("bf16_scoring_p32768" if fwd_only else "bf16_gqa_g16_p8192")]
     groups = groups_of(w)
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     log(f"[bench] workload {w.name}: {w.description}; T={w.total_rows}")
@@ -203,9 +220,9 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
     log(f"[bench] inputs on device in {time.perf_counter() - t0:.1f}s")
 
-    run = Runner(pg, torch, groups, w, tens)
+    run = Runner(pg, torch, groups, w, tens, forward_only=fwd_only)
     pairs, base_pairs = run.batch.pairs, run.batch.baseline_pairs
-    eff_flops = 14.0 * w.head_dim * w.num_q_heads * pairs
+    eff_flops = (4.0 if fwd_only else 14.0) * w.head_dim * w.num_q_heads * pairs
     ms, wall_ms, kern = run.timed(a.steps, a.warmup)
     value = eff_flops / (ms * 1e-3) / 1e12
     log(f"[bench] grouped: {ms:.3f} ms/step (host wall {wall_ms:.3f}), {value:.1f} TFLOP/s; "
@@ -256,7 +273,7 @@ def main(argv=None) -> int:
             t = s
         idx_t = torch.from_numpy(np.concatenate(idx)).to("cuda")
         btens = [x.index_select(0, idx_t).contiguous() for x in tens]
-        brun = Runner(pg, torch, bgroups, w, btens)
+        brun = Runner(pg, torch, bgroups, w, btens, forward_only=fwd_only)
         bsteps = max(2, a.steps // 4)
         base_ms, _, _ = brun.timed(bsteps, 1)
         speed = base_ms / ms
@@ -266,19 +283,21 @@ def main(argv=None) -> int:
 
     cpu = None
     if not a.no_cpu:
-        cpu = cpu_baseline(w, arrs, a.cpu_seconds)
+        cpu = cpu_baseline(w, arrs, a.cpu_seconds, forward_only=fwd_only)
         log(f"[bench] cpu baseline {cpu['value']:.4f} TFLOP/s on {cpu['cores']} threads")
 
     G = sum(len(rs) for _, rs in groups)
     res = {
-        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "metric": METRIC_FWD if fwd_only else METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic (seeded N(0,1) inputs, packed varlen layout)",
         "config": {"workload": w.name, "groups": [[P, rs] for P, rs in groups],
                    "num_q_heads": hq, "num_kv_heads": w.num_kv_heads, "head_dim": d,
                    "total_rows": T, "pairs_per_head": pairs, "baseline_pairs_per_head": base_pairs,
-                   "effective_flop_per_step": eff_flops, "step": "pg_pack + pg_attn_fwd + pg_attn_bwd"},
+                   "effective_flop_per_step": eff_flops,
+                   "step": ("pg_pack + pg_attn_fwd (no logsumexp)" if fwd_only
+                            else "pg_pack + pg_attn_fwd + pg_attn_bwd")},
         "pct_mfma_peak": round(100.0 * value / (PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS), 2),
         "speedup_vs_repeated_prefix": None if speed is None else round(speed, 3),
         "repeated_prefix_ms_per_step": None if base_ms is None else round(base_ms, 4),

@@ -157,7 +157,11 @@ pg_status pg_pack_host(const pg_groups *g, void *h_buf, size_t buf_bytes, int32_
  * query head.  softmax_scale <= 0 selects 1/sqrt(head_dim).  Prefix rows are
  * computed once per group (prefix-only causal attention); response rows
  * attend to the prefix and their own response (Pith review, "What carries the
- * argument").  q, k, v: input, o: output [T,Hq,d], lse: output float [Hq,T]. */
+ * argument").  q, k, v: input, o: output [T,Hq,d], lse: output float [Hq,T]
+ * (natural log), or NULL when no backward follows -- forward-only scoring of
+ * many short responses against one shared context, the other shared-prefix
+ * use the pages name (Pith review, "Editorial extensions"); O is then
+ * bitwise the same. */
 pg_status pg_attn_fwd(const pg_desc *d, pg_dtype t, float softmax_scale, const void *q,
                       const void *k, const void *v, void *o, float *lse, void *stream);
 

@@ -252,7 +252,8 @@ def repeated_prefix_rows(groups, q, k, v, do, q_rows, q_heads, scale=None) -> Di
     present in all G member sequences; its output is member 0's and its dQ
     is the sum over the G copies (each with dO / G), as in the full oracle.
     Cost per row is one softmax row of its sequence, so this works at any size.
-    Returns o [n_rows, n_heads, d], lse [n_heads, n_rows], dq like o.
+    Returns o [n_rows, n_heads, d], lse [n_heads, n_rows], dq like o (zeros
+    when do is None: forward only, one sequence per row).
     """
     T, hq, d = q.shape
     rep = hq // k.shape[1]
@@ -268,6 +269,8 @@ def repeated_prefix_rows(groups, q, k, v, do, q_rows, q_heads, scale=None) -> Di
             seqs = [members[owner[r]]]
         else:
             seqs = [m for m in members if m.prefix[0] <= r < m.prefix[1]]
+            if do is None:
+                seqs = seqs[:1]
         for hi, h in enumerate(q_heads):
             hk = h // rep
             for si, m in enumerate(seqs):
@@ -282,6 +285,8 @@ def repeated_prefix_rows(groups, q, k, v, do, q_rows, q_heads, scale=None) -> Di
                 if si == 0:
                     o[ri, hi] = p @ vv
                     lse[hi, ri] = l[0]
+                if do is None:
+                    continue
                 g = do[r, h].astype(np.float64) / len(seqs)
                 dp = vv @ g
                 ds = p * (dp - (p * dp).sum())

@@ -241,7 +241,8 @@ def _scale(s) -> float:
 
 
 def pg_attn_fwd(batch: PackedBatch, q, k, v, softmax_scale: Optional[float] = None, out=None,
-                lse=None):
+                lse=None, store_lse: bool = True):
+    """O (and LSE unless store_lse is False: forward-only scoring, lse is None)."""
     torch = _torch()
     d = batch.desc
     T, hq, hkv, D = d.total_rows, d.num_q_heads, d.num_kv_heads, d.head_dim
@@ -250,11 +251,14 @@ def pg_attn_fwd(batch: PackedBatch, q, k, v, softmax_scale: Optional[float] = No
     _check_tensor("k", k, (T, hkv, D), q.dtype, dev)
     _check_tensor("v", v, (T, hkv, D), q.dtype, dev)
     o = torch.empty_like(q) if out is None else out
-    l = torch.empty((hq, T), dtype=torch.float32, device=dev) if lse is None else lse
     _check_tensor("o", o, (T, hq, D), q.dtype, dev)
-    _check_tensor("lse", l, (hq, T), torch.float32, dev)
+    l = None
+    if store_lse:
+        l = torch.empty((hq, T), dtype=torch.float32, device=dev) if lse is None else lse
+        _check_tensor("lse", l, (hq, T), torch.float32, dev)
     _check(lib().pg_attn_fwd(ctypes.byref(d), _dtype_code(q.dtype), _scale(softmax_scale),
-                             _vp(q), _vp(k), _vp(v), _vp(o), _vp(l), _stream_ptr(dev)))
+                             _vp(q), _vp(k), _vp(v), _vp(o), _vp(l) if l is not None else None,
+                             _stream_ptr(dev)))
     return o, l
 
 

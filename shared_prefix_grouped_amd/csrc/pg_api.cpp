@@ -412,7 +412,8 @@ pg_status pg_attn_fwd(const pg_desc *d, pg_dtype t, float softmax_scale, const v
   if (st != PG_OK) return st;
   if ((st = check_dtype(t)) != PG_OK) return st;
   if (d->total_rows == 0) return PG_OK;
-  if ((st = check_ptrs({{q, "q"}, {k, "k"}, {v, "v"}, {o, "o"}, {lse, "lse"}})) != PG_OK) return st;
+  if ((st = check_ptrs({{q, "q"}, {k, "k"}, {v, "v"}, {o, "o"}})) != PG_OK) return st;
+  if (lse != nullptr && (st = check_ptrs({{lse, "lse"}})) != PG_OK) return st;
   pg::Plan p = plan_of(d);
   const float scale = resolve_scale(softmax_scale, p.D);
   hipStream_t s = static_cast<hipStream_t>(stream);

@@ -82,7 +82,7 @@ __global__ __launch_bounds__(kF32Threads) void fwd_f32_kernel(
   float *op = O + ((size_t)qrow * Hq + h) * D + c0;
 #pragma unroll
   for (int c = 0; c < DH; ++c) op[c] = acc[c] * inv;
-  if (c0 == 0) LSE[(size_t)h * T + qrow] = (m + __log2f(l)) * kLn2;
+  if (LSE != nullptr && c0 == 0) LSE[(size_t)h * T + qrow] = (m + __log2f(l)) * kLn2;
 }
 
 template <int D>

@@ -218,7 +218,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
           pack4_bf16(o[nb][rq * 4 + 0] * inv, o[nb][rq * 4 + 1] * inv, o[nb][rq * 4 + 2] * inv,
                      o[nb][rq * 4 + 3] * inv);
     }
-  if (hi == 0) LSE[(size_t)h * T + qrow] = (m + __log2f(lt)) * kLn2;
+  if (LSE != nullptr && hi == 0) LSE[(size_t)h * T + qrow] = (m + __log2f(lt)) * kLn2;
 }
 
 }  // namespace

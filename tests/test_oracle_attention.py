@@ -357,3 +357,19 @@ def test_kv_head_subset_matches_full():
     assert list(sub["q_heads"]) == [2, 3]
     assert np.allclose(sub["o"], full["o"][:, 2:4], atol=0, rtol=0)
     assert np.allclose(sub["dk"][:, 0], full["dk"][:, 1], atol=0, rtol=0)
+
+
+def test_sampled_rows_forward_only_matches_full_oracle():
+    """do=None (forward only) gives the same O and LSE as the full oracle."""
+    from oracle.attention import repeated_prefix_rows
+    groups = [(5, [3, 0, 4]), (2, [2])]
+    rng = np.random.default_rng(21)
+    members, T = member_sequences(groups)
+    q = rng.standard_normal((T, 2, 8)); k = rng.standard_normal((T, 1, 8))
+    v = rng.standard_normal((T, 1, 8)); do = rng.standard_normal((T, 2, 8))
+    full = repeated_prefix_attention(groups, q, k, v, do)
+    rows = list(range(T))
+    fwd = repeated_prefix_rows(groups, q, k, v, None, rows, [0, 1])
+    assert np.allclose(fwd["o"], full["o"][rows][:, [0, 1]], atol=1e-12, rtol=0)
+    assert np.allclose(fwd["lse"], full["lse"][[0, 1]][:, rows], atol=1e-12, rtol=0)
+    assert not fwd["dq"].any()

@@ -91,7 +91,8 @@ def _ragged(rng: np.random.Generator, lo: int, hi: int, n: int) -> Tuple[int, ..
 
 
 def attention_workloads() -> Dict[str, AttnWorkload]:
-    """The four attention workloads, keyed by a short name.
+    """The attention workloads, keyed by a short name (the last one is scored
+    forward-only: many short responses against one long shared context).
 
     The ragged lengths are drawn from the same generator that then draws the
     tensors (see ``draw_attention_inputs``), so they are recomputed here with
@@ -114,6 +115,9 @@ def attention_workloads() -> Dict[str, AttnWorkload]:
         "bf16_varlen_2groups", "bf16",
         (Group(32768, (512,) * 8), Group(2048, _ragged(rng, 128, 2048, 8))), 64, 8, 128, seed=4,
         description="bf16, GQA 64/8, groups (P=32768, 8x512) + (P=2048, 8 responses in [128,2048]), d=128")
+    out["bf16_scoring_p32768"] = AttnWorkload(
+        "bf16_scoring_p32768", "bf16", (Group(32768, (32,) * 64),), 32, 8, 128, seed=6,
+        description="bf16 forward-only scoring: GQA 32/8, 1 group, P=32768, 64 responses of 32, d=128")
     return out
 
 
