@@ -7,6 +7,12 @@ One step is one pass of the whole path over one packed batch with inputs
 already resident in HBM: pg_pack (plan + descriptor upload), pg_attn_fwd and
 pg_attn_bwd.  Prints ONE JSON line on stdout; progress goes to stderr.
 
+--ratio-sweep  the pages' prefix/response ratio experiment: G = 16 responses
+           of 256 rows, P = ratio * 256 for ratio 0.5 .. 64, bf16 GQA 32/8,
+           d = 128; per point the fwd+bwd step time of the grouped and of the
+           repeated-prefix layout (same kernels), their ratio beside the exact
+           attention-FLOP ratio pairs_g / pairs_b and its limit 1/G, and the
+           bytes of the path's tensors in each layout.  One JSON line.
 --forward-only  scoring mode: a step is pg_pack + pg_attn_fwd without the
            logsumexp store (many short responses scored against one long
            context; default workload bf16_scoring_p32768); value is then
@@ -60,6 +66,8 @@ def parse(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=None,
                     help="bf16_gqa_g16_p8192 (default), or bf16_scoring_p32768 with --forward-only")
+    ap.add_argument("--ratio-sweep", action="store_true",
+                    help="time grouped vs repeated-prefix layouts over prefix/response ratios")
     ap.add_argument("--forward-only", action="store_true",
                     help="score without backward and without storing the logsumexp")
     ap.add_argument("--no-baseline", action="store_true", help="skip the repeated-prefix run")
@@ -195,6 +203,51 @@ def cpu_baseline(w, arrs, budget_s, forward_only=False):
     }
 
 
+def path_bytes(T, hq, hkv, d, esize=2):
+    """Bytes of the path's tensors for T packed rows: q, o, dO, dQ [T, Hq, d];
+    k, v, dK, dV [T, Hkv, d]; logsumexp, delta and the base-2 logsumexp [Hq, T]."""
+    return 4 * T * hq * d * esize + 4 * T * hkv * d * esize + 3 * hq * T * 4
+
+
+def ratio_sweep(a, pg, torch) -> dict:
+    G, R, hq, hkv, d = 16, 256, 32, 8, 128
+    ratios = [0.5, 1, 2, 4, 8, 16, 32, 64]
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    points = []
+    for ratio in ratios:
+        P = int(ratio * R)
+        groups = [(P, [R] * G)]
+        T = P + G * R
+        w = type("W", (), {"num_q_heads": hq, "num_kv_heads": hkv, "head_dim": d})()
+        tens = [torch.randn((T, h, d), generator=gen, device="cuda").to(torch.bfloat16)
+                for h in (hq, hkv, hkv, hq)]
+        run = Runner(pg, torch, groups, w, tens)
+        g_ms, _, _ = run.timed(max(2, a.steps // 4), 2)
+        pairs, base_pairs = run.batch.pairs, run.batch.baseline_pairs
+        idx = np.concatenate([np.concatenate([np.arange(P), np.arange(P + i * R, P + (i + 1) * R)])
+                              for i in range(G)])
+        idx_t = torch.from_numpy(idx).to("cuda")
+        btens = [x.index_select(0, idx_t).contiguous() for x in tens]
+        del run
+        brun = Runner(pg, torch, [(P, [R])] * G, w, btens)
+        b_ms, _, _ = brun.timed(max(2, a.steps // 4), 1)
+        del brun, btens, tens
+        torch.cuda.empty_cache()
+        pt = {"ratio": ratio, "prefix": P, "grouped_ms": round(g_ms, 4), "repeated_prefix_ms": round(b_ms, 4),
+              "time_ratio": round(g_ms / b_ms, 4), "attn_flop_ratio": round(pairs / base_pairs, 4),
+              "grouped_tflops": round(14.0 * d * hq * pairs / (g_ms * 1e-3) / 1e12, 1),
+              "bytes_ratio": round(path_bytes(T, hq, hkv, d) / path_bytes(G * (P + R), hq, hkv, d), 4),
+              "grouped_bytes": path_bytes(T, hq, hkv, d), "repeated_prefix_bytes": path_bytes(G * (P + R), hq, hkv, d)}
+        log(f"[sweep] ratio {ratio}: grouped {g_ms:.3f} ms, repeated-prefix {b_ms:.3f} ms, time ratio "
+            f"{pt['time_ratio']:.3f}, FLOP ratio {pt['attn_flop_ratio']:.3f}, bytes ratio {pt['bytes_ratio']:.3f}")
+        points.append(pt)
+    return {"metric": "grouped / repeated-prefix fwd+bwd time vs prefix/response ratio", "n_gpus": 1,
+            "dtype": "bf16", "data": "synthetic (seeded N(0,1) inputs)",
+            "config": {"workload": "ratio_sweep", "G": G, "response_len": R, "num_q_heads": hq,
+                       "num_kv_heads": hkv, "head_dim": d, "limit_1_over_G": round(1.0 / G, 4)},
+            "points": points}
+
+
 def main(argv=None) -> int:
     a = parse(argv)
     if a.gpus != 1:
@@ -209,6 +262,9 @@ def main(argv=None) -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
     pg.lib()  # fails loudly when the HIP library is not built
+    if a.ratio_sweep:
+        print(json.dumps(ratio_sweep(a, pg, torch)), flush=True)
+        return 0
     fwd_only = a.forward_only
     w = attention_workloads()[a.workload or ("bf16_scoring_p32768" if fwd_only else "bf16_gqa_g16_p8192")]
     groups = groups_of(w)
