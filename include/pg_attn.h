@@ -110,6 +110,19 @@ typedef struct {
  *   kv_tiles     [num_kv_tiles][4] = {k0, k1, q_end, prefix end}: key rows
  *                [k0, k1) of one group, k1 - k0 <= PG_TILE_KV, seen by query
  *                rows inside [k0, q_end), ordered by decreasing cost.
+ *   kv_items     [num_kv_items][8] = {k0, k1, qa, qb, part, 0, 0, 0}: the bf16
+ *                dK/dV work list, ordered by decreasing cost.  Key tile
+ *                [k0, k1) against query rows [qa, qb).  part < 0: the whole
+ *                tile (qa = k0, qb = q_end).  part >= 0: one piece of a tile
+ *                whose walk was cut at 32-row query blocks (qa - k0 a multiple
+ *                of 32), because it alone held more than the mean work per
+ *                compute unit -- the prefix tiles of a group with a short
+ *                prefix and many responses; its float partial dK/dV goes to
+ *                workspace slot `part`.
+ *   kv_sums      [num_kv_sums][4] = {k0, k1, first part, number of parts}:
+ *                the cut tiles; their parts are consecutive and are added in
+ *                part order, so the result does not depend on scheduling.
+ *                num_kv_parts = total number of parts.
  *   group_start  [num_groups + 1], prefix_end [num_groups],
  *   resp_start   [num_resp], resp_len [num_resp], resp_group [num_resp]:
  *                the packed offsets, for callers.
@@ -120,11 +133,14 @@ typedef struct {
   int32_t num_groups, num_resp, total_rows;
   int32_t num_q_heads, num_kv_heads, head_dim;
   int32_t num_q_tiles, num_kv_tiles;
+  int32_t num_kv_items, num_kv_sums, num_kv_parts;
   int64_t pairs, baseline_pairs;
   const int32_t *row_lo;
   const int32_t *row_hi;
   const int32_t *q_tiles;
   const int32_t *kv_tiles;
+  const int32_t *kv_items;
+  const int32_t *kv_sums;
   const int32_t *group_start;
   const int32_t *prefix_end;
   const int32_t *resp_start;
@@ -166,7 +182,9 @@ pg_status pg_attn_fwd(const pg_desc *d, pg_dtype t, float softmax_scale, const v
                       const void *k, const void *v, void *o, float *lse, void *stream);
 
 /* Bytes of scratch pg_attn_bwd needs: two float [Hq, T] arrays, rowsum(dO * O)
- * and the logsumexp in base 2, each 16-byte aligned. */
+ * and the logsumexp in base 2, each 16-byte aligned, and for PG_BF16 the
+ * partial dK/dV sums of the cut key tiles, float
+ * [num_kv_parts][num_kv_heads][2][PG_TILE_KV][head_dim]. */
 size_t pg_attn_bwd_workspace_size(const pg_desc *d, pg_dtype t);
 
 /* Backward: gradients of sum(O * dO) with respect to Q, K, V, recomputing the
@@ -176,7 +194,10 @@ size_t pg_attn_bwd_workspace_size(const pg_desc *d, pg_dtype t);
  * "Core claim", Lemma 2.1).  Inputs q, k, v, o, lse, dout as produced by /
  * given to pg_attn_fwd; outputs dq [T,Hq,d], dk, dv [T,Hkv,d] are fully
  * overwritten.  `workspace` is device scratch of at least
- * pg_attn_bwd_workspace_size bytes (contents need not be initialised). */
+ * pg_attn_bwd_workspace_size bytes (contents need not be initialised).
+ * PG_BF16 needs (T + 32) * Hq * d * 2 < 2^31 (q and dout under 2 GiB each:
+ * the dK/dV kernel addresses them with 32-bit signed buffer offsets), else
+ * PG_ERR_UNSUPPORTED. */
 pg_status pg_attn_bwd(const pg_desc *d, pg_dtype t, float softmax_scale, const void *q,
                       const void *k, const void *v, const void *o, const float *lse,
                       const void *dout, void *dq, void *dk, void *dv, void *workspace,

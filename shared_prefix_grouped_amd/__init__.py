@@ -64,8 +64,11 @@ class PgDesc(ctypes.Structure):
                 ("total_rows", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
                 ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("num_q_tiles", ctypes.c_int32), ("num_kv_tiles", ctypes.c_int32),
+                ("num_kv_items", ctypes.c_int32), ("num_kv_sums", ctypes.c_int32),
+                ("num_kv_parts", ctypes.c_int32),
                 ("pairs", ctypes.c_int64), ("baseline_pairs", ctypes.c_int64),
                 ("row_lo", _i32p), ("row_hi", _i32p), ("q_tiles", _i32p), ("kv_tiles", _i32p),
+                ("kv_items", _i32p), ("kv_sums", _i32p),
                 ("group_start", _i32p), ("prefix_end", _i32p), ("resp_start", _i32p),
                 ("resp_len", _i32p), ("resp_group", _i32p), ("buf_bytes", ctypes.c_size_t)]
 
@@ -205,6 +208,8 @@ def pg_pack_host(groups: Sequence, num_q_heads: int, num_kv_heads: int, head_dim
         "num_q_tiles": d.num_q_tiles, "num_kv_tiles": d.num_kv_tiles,
         "row_lo": arr(d.row_lo, T), "row_hi": arr(d.row_hi, T),
         "q_tiles": arr(d.q_tiles, d.num_q_tiles, 4), "kv_tiles": arr(d.kv_tiles, d.num_kv_tiles, 4),
+        "kv_items": arr(d.kv_items, d.num_kv_items, 8), "kv_sums": arr(d.kv_sums, d.num_kv_sums, 4),
+        "num_kv_parts": d.num_kv_parts,
         "group_start": arr(d.group_start, d.num_groups + 1), "prefix_end": arr(d.prefix_end, d.num_groups),
         "resp_start": arr(d.resp_start, d.num_resp), "resp_len": arr(d.resp_len, d.num_resp),
         "resp_group": arr(d.resp_group, d.num_resp), "pos_ids": pos[:T].copy(),

@@ -36,11 +36,12 @@ size_t align16(size_t x) { return (x + 15) & ~size_t(15); }
 
 // Byte offsets of each array inside the descriptor buffer.
 struct Layout {
-  size_t row_lo, row_hi, q_tiles, kv_tiles, group_start, prefix_end, resp_start, resp_len,
-      resp_group, total;
+  size_t row_lo, row_hi, q_tiles, kv_tiles, kv_items, kv_sums, group_start, prefix_end,
+      resp_start, resp_len, resp_group, total;
 };
 
-Layout make_layout(int64_t T, int64_t n_groups, int64_t n_resp, int64_t n_qt, int64_t n_kvt) {
+Layout make_layout(int64_t T, int64_t n_groups, int64_t n_resp, int64_t n_qt, int64_t n_kvt,
+                   int64_t n_items, int64_t n_sums) {
   Layout L{};
   size_t off = 0;
   auto take = [&](size_t &field, int64_t n_int32) {
@@ -51,6 +52,8 @@ Layout make_layout(int64_t T, int64_t n_groups, int64_t n_resp, int64_t n_qt, in
   take(L.row_hi, T);
   take(L.q_tiles, 4 * n_qt);
   take(L.kv_tiles, 4 * n_kvt);
+  take(L.kv_items, 8 * n_items);
+  take(L.kv_sums, 4 * n_sums);
   take(L.group_start, n_groups + 1);
   take(L.prefix_end, n_groups);
   take(L.resp_start, n_resp);
@@ -62,9 +65,8 @@ Layout make_layout(int64_t T, int64_t n_groups, int64_t n_resp, int64_t n_qt, in
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Validate a pg_groups and compute the sizes that do not need the full plan.
-pg_status check_groups(const pg_groups *g, int64_t *T_out, int64_t *n_resp_out,
-                       int64_t *n_qt_out, int64_t *n_kvt_out) {
+// Validate a pg_groups and compute the total row count.
+pg_status check_groups(const pg_groups *g, int64_t *T_out, int64_t *n_resp_out) {
   if (!g) return fail(PG_ERR_INVALID_ARG, "pg_groups is NULL");
   if (g->num_groups < 0) return fail(PG_ERR_INVALID_ARG, "num_groups < 0");
   if (g->num_groups > 0 && (!g->prefix_len || !g->num_resp || !g->resp_len))
@@ -75,7 +77,7 @@ pg_status check_groups(const pg_groups *g, int64_t *T_out, int64_t *n_resp_out,
     return fail(PG_ERR_INVALID_ARG, "num_q_heads must be a multiple of num_kv_heads");
   if (g->head_dim != 64 && g->head_dim != 128)
     return fail(PG_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
-  int64_t T = 0, n_resp = 0, n_qt = 0, n_kvt = 0;
+  int64_t T = 0, n_resp = 0;
   for (int32_t i = 0; i < g->num_groups; ++i) {
     if (g->prefix_len[i] < 0) return fail(PG_ERR_INVALID_ARG, "prefix_len < 0 in group " + std::to_string(i));
     if (g->num_resp[i] < 1) return fail(PG_ERR_INVALID_ARG, "num_resp < 1 in group " + std::to_string(i));
@@ -88,15 +90,11 @@ pg_status check_groups(const pg_groups *g, int64_t *T_out, int64_t *n_resp_out,
     n_resp += g->num_resp[i];
     T += rows;
     if (T > INT32_MAX / 2) return fail(PG_ERR_INVALID_ARG, "total rows exceed the int32 range");
-    n_qt += ceil_div(rows, PG_TILE_Q);
-    n_kvt += ceil_div(rows, PG_TILE_KV);
   }
   if (T * int64_t(g->num_q_heads) * g->head_dim > (int64_t(1) << 40))
     return fail(PG_ERR_INVALID_ARG, "tensor too large");
   *T_out = T;
   *n_resp_out = n_resp;
-  *n_qt_out = n_qt;
-  *n_kvt_out = n_kvt;
   return PG_OK;
 }
 
@@ -106,55 +104,81 @@ struct Tile {
   int64_t order;
 };
 
-// Build the whole plan into `buf` (host memory of at least L.total bytes).
-pg_status build_plan(const pg_groups *g, char *buf, size_t buf_bytes, int32_t *pos_ids,
-                     pg_desc *out, Layout *L_out) {
-  int64_t T, n_resp, n_qt, n_kvt;
-  pg_status st = check_groups(g, &T, &n_resp, &n_qt, &n_kvt);
-  if (st != PG_OK) return st;
-  Layout L = make_layout(T, g->num_groups, n_resp, n_qt, n_kvt);
-  if (buf_bytes < L.total)
-    return fail(PG_ERR_WORKSPACE, "descriptor buffer too small: need " + std::to_string(L.total) +
-                                      " bytes, got " + std::to_string(buf_bytes));
-  std::memset(buf, 0, L.total);
-  auto arr = [&](size_t off) { return reinterpret_cast<int32_t *>(buf + off); };
-  int32_t *row_lo = arr(L.row_lo), *row_hi = arr(L.row_hi);
-  int32_t *gstart = arr(L.group_start), *pend = arr(L.prefix_end);
-  int32_t *rstart = arr(L.resp_start), *rlen = arr(L.resp_len), *rgroup = arr(L.resp_group);
+// One dK/dV work item: key rows [k0, k1) against query rows [qa, qb).
+struct KvItem {
+  int32_t k0, k1, qa, qb, part;
+  int64_t cost;
+  int64_t order;
+};
 
+// Splitting of long dK/dV walks.  A key tile is seen by every query row from
+// its own rows to the end of its visibility range; for a prefix tile that is
+// the rest of the prefix and every response of the group, so a short prefix
+// with many responses leaves a few key tiles with nearly all the work.  Such a
+// tile is cut into pieces of whole 32-row query blocks, each its own
+// workgroup, whose float partial sums a second kernel adds in piece order.
+// A tile is cut when its work exceeds the mean per workgroup slot (one dK/dV
+// workgroup is resident per compute unit; an MI355X has 256), into pieces of
+// at least kMinPieceSteps (query head, 32-row block) steps so that the fixed
+// cost of a piece (its K/V rows, pipeline fill, partial write and re-read)
+// stays small beside its walk.
+constexpr int64_t kDkdvSlots = 256;
+constexpr int kMinPieceSteps = 32;
+constexpr int kQueryBlock = 32;
+
+// The complete plan in host memory, before it is laid out in one buffer.
+struct HostPlan {
+  int64_t T = 0, n_resp = 0, pairs = 0, base_pairs = 0;
+  int32_t n_parts = 0;
+  std::vector<int32_t> row_lo, row_hi, pos, gstart, pend, rstart, rlen, rgroup;
   std::vector<Tile> qt, kvt;
-  qt.reserve(n_qt);
-  kvt.reserve(n_kvt);
-  int64_t pairs = 0, base_pairs = 0;
+  std::vector<KvItem> items;
+  std::vector<int32_t> sums;  // 4 per split tile
+};
+
+pg_status plan_batch(const pg_groups *g, HostPlan &hp) {
+  pg_status st = check_groups(g, &hp.T, &hp.n_resp);
+  if (st != PG_OK) return st;
+  const int64_t T = hp.T;
+  hp.row_lo.assign(T, 0);
+  hp.row_hi.assign(T, 0);
+  hp.pos.assign(T, 0);
+  hp.gstart.assign(g->num_groups + 1, 0);
+  hp.pend.assign(g->num_groups, 0);
+  hp.rstart.assign(hp.n_resp, 0);
+  hp.rlen.assign(hp.n_resp, 0);
+  hp.rgroup.assign(hp.n_resp, 0);
+  int32_t *row_lo = hp.row_lo.data(), *row_hi = hp.row_hi.data();
+  std::vector<Tile> &qt = hp.qt, &kvt = hp.kvt;
   int32_t t = 0, ri = 0;
   for (int32_t gi = 0; gi < g->num_groups; ++gi) {
     const int32_t P = g->prefix_len[gi];
     const int32_t g0 = t, pe = t + P;
-    gstart[gi] = g0;
-    pend[gi] = pe;
+    hp.gstart[gi] = g0;
+    hp.pend[gi] = pe;
     int32_t gend = pe;
     for (int32_t r = 0; r < g->num_resp[gi]; ++r) gend += g->resp_len[ri + r];
     // prefix rows: own segment is the prefix itself; seen by every later row of the group
     for (int32_t x = g0; x < pe; ++x) {
       row_lo[x] = g0;
       row_hi[x] = gend;
-      if (pos_ids) pos_ids[x] = x - g0;
+      hp.pos[x] = x - g0;
     }
-    pairs += int64_t(P) * (P + 1) / 2;
+    hp.pairs += int64_t(P) * (P + 1) / 2;
     int32_t s = pe;
     for (int32_t r = 0; r < g->num_resp[gi]; ++r, ++ri) {
       const int32_t R = g->resp_len[ri];
-      rstart[ri] = s;
-      rlen[ri] = R;
-      rgroup[ri] = gi;
+      hp.rstart[ri] = s;
+      hp.rlen[ri] = R;
+      hp.rgroup[ri] = gi;
       for (int32_t x = s; x < s + R; ++x) {
         row_lo[x] = s;
         row_hi[x] = s + R;
-        if (pos_ids) pos_ids[x] = P + (x - s);
+        hp.pos[x] = P + (x - s);
       }
-      pairs += int64_t(R) * P + int64_t(R) * (R + 1) / 2;
+      hp.pairs += int64_t(R) * P + int64_t(R) * (R + 1) / 2;
       const int64_t Lb = int64_t(P) + R;
-      base_pairs += Lb * (Lb + 1) / 2;
+      hp.base_pairs += Lb * (Lb + 1) / 2;
       s += R;
     }
     // query tiles: cost = number of visible keys summed over the tile's rows
@@ -178,41 +202,107 @@ pg_status build_plan(const pg_groups *g, char *buf, size_t buf_bytes, int32_t *p
     }
     t = gend;
   }
-  gstart[g->num_groups] = t;
+  hp.gstart[g->num_groups] = t;
+
+  // dK/dV work items (packed order), cutting the tiles whose walk is too long
+  int64_t total = 0;
+  for (const Tile &k : kvt) total += k.cost;
+  const int rep = g->num_q_heads / g->num_kv_heads;
+  const int64_t cap = std::max<int64_t>(1, ceil_div(total * g->num_kv_heads, kDkdvSlots));
+  const int64_t min_blocks = ceil_div(kMinPieceSteps, rep);
+  for (const Tile &k : kvt) {
+    const int32_t k0 = k.a, k1 = k.b, qend = k.c;
+    const int64_t nblk = ceil_div(qend - k0, kQueryBlock);
+    int64_t pieces = 1;
+    if (k.cost > cap) pieces = std::max<int64_t>(1, std::min(ceil_div(k.cost, cap), nblk / min_blocks));
+    if (pieces == 1) {
+      hp.items.push_back({k0, k1, k0, qend, -1, k.cost, 0});
+      continue;
+    }
+    hp.sums.insert(hp.sums.end(), {k0, k1, hp.n_parts, int32_t(pieces)});
+    for (int64_t j = 0; j < pieces; ++j) {
+      const int32_t qa = k0 + int32_t(j * nblk / pieces) * kQueryBlock;
+      const int32_t qb = (j + 1 == pieces) ? qend : k0 + int32_t((j + 1) * nblk / pieces) * kQueryBlock;
+      int64_t cost = 0;  // pairs of the piece: key x is seen by queries [x, row_hi[x])
+      for (int32_t x = k0; x < k1; ++x)
+        cost += std::max<int64_t>(0, int64_t(std::min(row_hi[x], qb)) - std::max(x, qa));
+      hp.items.push_back({k0, k1, qa, qb, hp.n_parts++, cost, 0});
+    }
+  }
+  for (size_t i = 0; i < hp.items.size(); ++i) hp.items[i].order = int64_t(i);
+
   // longest-processing-time-first order; ties keep packed order
-  auto by_cost = [](const Tile &x, const Tile &y) {
+  auto by_cost = [](const auto &x, const auto &y) {
     return x.cost != y.cost ? x.cost > y.cost : x.order < y.order;
   };
   std::sort(qt.begin(), qt.end(), by_cost);
   std::sort(kvt.begin(), kvt.end(), by_cost);
-  int32_t *qa = arr(L.q_tiles), *ka = arr(L.kv_tiles);
-  for (size_t i = 0; i < qt.size(); ++i) {
-    qa[4 * i + 0] = qt[i].a;
-    qa[4 * i + 1] = qt[i].b;
-    qa[4 * i + 2] = qt[i].c;
-    qa[4 * i + 3] = qt[i].d;
+  std::sort(hp.items.begin(), hp.items.end(), by_cost);
+  return PG_OK;
+}
+
+Layout layout_of(const pg_groups *g, const HostPlan &hp) {
+  return make_layout(hp.T, g->num_groups, hp.n_resp, int64_t(hp.qt.size()), int64_t(hp.kvt.size()),
+                     int64_t(hp.items.size()), int64_t(hp.sums.size() / 4));
+}
+
+// Lay the plan out in `buf` (host memory of at least L.total bytes).
+void serialize(const pg_groups *g, const HostPlan &hp, const Layout &L, char *buf,
+               int32_t *pos_ids, pg_desc *out) {
+  std::memset(buf, 0, L.total);
+  auto put = [&](size_t off, const std::vector<int32_t> &v) {
+    if (!v.empty()) std::memcpy(buf + off, v.data(), v.size() * 4);
+  };
+  put(L.row_lo, hp.row_lo);
+  put(L.row_hi, hp.row_hi);
+  put(L.kv_sums, hp.sums);
+  put(L.group_start, hp.gstart);
+  put(L.prefix_end, hp.pend);
+  put(L.resp_start, hp.rstart);
+  put(L.resp_len, hp.rlen);
+  put(L.resp_group, hp.rgroup);
+  if (pos_ids && hp.T > 0) std::memcpy(pos_ids, hp.pos.data(), size_t(hp.T) * 4);
+  auto arr = [&](size_t off) { return reinterpret_cast<int32_t *>(buf + off); };
+  int32_t *qa = arr(L.q_tiles), *ka = arr(L.kv_tiles), *ia = arr(L.kv_items);
+  for (size_t i = 0; i < hp.qt.size(); ++i) {
+    const Tile &x = hp.qt[i];
+    qa[4 * i + 0] = x.a;
+    qa[4 * i + 1] = x.b;
+    qa[4 * i + 2] = x.c;
+    qa[4 * i + 3] = x.d;
   }
-  for (size_t i = 0; i < kvt.size(); ++i) {
-    ka[4 * i + 0] = kvt[i].a;
-    ka[4 * i + 1] = kvt[i].b;
-    ka[4 * i + 2] = kvt[i].c;
-    ka[4 * i + 3] = kvt[i].d;
+  for (size_t i = 0; i < hp.kvt.size(); ++i) {
+    const Tile &x = hp.kvt[i];
+    ka[4 * i + 0] = x.a;
+    ka[4 * i + 1] = x.b;
+    ka[4 * i + 2] = x.c;
+    ka[4 * i + 3] = x.d;
+  }
+  for (size_t i = 0; i < hp.items.size(); ++i) {
+    const KvItem &x = hp.items[i];
+    int32_t *e = ia + 8 * i;
+    e[0] = x.k0;
+    e[1] = x.k1;
+    e[2] = x.qa;
+    e[3] = x.qb;
+    e[4] = x.part;
   }
   pg_desc d{};
   d.num_groups = g->num_groups;
-  d.num_resp = int32_t(n_resp);
-  d.total_rows = int32_t(T);
+  d.num_resp = int32_t(hp.n_resp);
+  d.total_rows = int32_t(hp.T);
   d.num_q_heads = g->num_q_heads;
   d.num_kv_heads = g->num_kv_heads;
   d.head_dim = g->head_dim;
-  d.num_q_tiles = int32_t(qt.size());
-  d.num_kv_tiles = int32_t(kvt.size());
-  d.pairs = pairs;
-  d.baseline_pairs = base_pairs;
+  d.num_q_tiles = int32_t(hp.qt.size());
+  d.num_kv_tiles = int32_t(hp.kvt.size());
+  d.num_kv_items = int32_t(hp.items.size());
+  d.num_kv_sums = int32_t(hp.sums.size() / 4);
+  d.num_kv_parts = hp.n_parts;
+  d.pairs = hp.pairs;
+  d.baseline_pairs = hp.base_pairs;
   d.buf_bytes = L.total;
   *out = d;
-  *L_out = L;
-  return PG_OK;
 }
 
 void point_into(pg_desc *d, const Layout &L, const char *base) {
@@ -221,6 +311,8 @@ void point_into(pg_desc *d, const Layout &L, const char *base) {
   d->row_hi = p(L.row_hi);
   d->q_tiles = p(L.q_tiles);
   d->kv_tiles = p(L.kv_tiles);
+  d->kv_items = p(L.kv_items);
+  d->kv_sums = p(L.kv_sums);
   d->group_start = p(L.group_start);
   d->prefix_end = p(L.prefix_end);
   d->resp_start = p(L.resp_start);
@@ -231,11 +323,13 @@ void point_into(pg_desc *d, const Layout &L, const char *base) {
 pg_status check_desc(const pg_desc *d) {
   if (!d) return fail(PG_ERR_INVALID_ARG, "pg_desc is NULL");
   if (d->total_rows < 0 || d->num_q_heads <= 0 || d->num_kv_heads <= 0 ||
-      d->num_q_heads % d->num_kv_heads || d->num_q_tiles < 0 || d->num_kv_tiles < 0)
+      d->num_q_heads % d->num_kv_heads || d->num_q_tiles < 0 || d->num_kv_tiles < 0 ||
+      d->num_kv_items < 0 || d->num_kv_sums < 0 || d->num_kv_parts < 0)
     return fail(PG_ERR_INVALID_ARG, "descriptor is not one filled by pg_pack");
   if (d->head_dim != 64 && d->head_dim != 128)
     return fail(PG_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
-  if (d->total_rows > 0 && (!d->row_lo || !d->row_hi || !d->q_tiles || !d->kv_tiles))
+  if (d->total_rows > 0 &&
+      (!d->row_lo || !d->row_hi || !d->q_tiles || !d->kv_tiles || !d->kv_items || !d->kv_sums))
     return fail(PG_ERR_INVALID_ARG, "descriptor arrays are NULL");
   return PG_OK;
 }
@@ -266,6 +360,11 @@ pg::Plan plan_of(const pg_desc *d) {
   p.row_hi = d->row_hi;
   p.q_tiles = d->q_tiles;
   p.kv_tiles = d->kv_tiles;
+  p.n_kv_items = d->num_kv_items;
+  p.n_kv_sums = d->num_kv_sums;
+  p.n_kv_parts = d->num_kv_parts;
+  p.kv_items = d->kv_items;
+  p.kv_sums = d->kv_sums;
   return p;
 }
 
@@ -360,18 +459,23 @@ hipError_t timed(int id, hipStream_t s, F &&launch) {
 extern "C" {
 
 size_t pg_pack_buffer_size(const pg_groups *g) {
-  int64_t T, n_resp, n_qt, n_kvt;
-  if (check_groups(g, &T, &n_resp, &n_qt, &n_kvt) != PG_OK) return 0;
-  return make_layout(T, g->num_groups, n_resp, n_qt, n_kvt).total;
+  HostPlan hp;
+  if (plan_batch(g, hp) != PG_OK) return 0;
+  return layout_of(g, hp).total;
 }
 
 pg_status pg_pack_host(const pg_groups *g, void *h_buf, size_t buf_bytes, int32_t *h_pos_ids,
                        pg_desc *out) {
   if (!h_buf || !out) return fail(PG_ERR_INVALID_ARG, "h_buf and out must not be NULL");
-  Layout L;
-  pg_desc d;
-  pg_status st = build_plan(g, static_cast<char *>(h_buf), buf_bytes, h_pos_ids, &d, &L);
+  HostPlan hp;
+  pg_status st = plan_batch(g, hp);
   if (st != PG_OK) return st;
+  const Layout L = layout_of(g, hp);
+  if (buf_bytes < L.total)
+    return fail(PG_ERR_WORKSPACE, "descriptor buffer too small: need " + std::to_string(L.total) +
+                                      " bytes, got " + std::to_string(buf_bytes));
+  pg_desc d;
+  serialize(g, hp, L, static_cast<char *>(h_buf), h_pos_ids, &d);
   point_into(&d, L, static_cast<const char *>(h_buf));
   *out = d;
   return PG_OK;
@@ -381,23 +485,21 @@ pg_status pg_pack(const pg_groups *g, void *d_buf, size_t buf_bytes, int32_t *d_
                   pg_desc *out, void *stream) {
   if (!d_buf || !out) return fail(PG_ERR_INVALID_ARG, "d_buf and out must not be NULL");
   if (!aligned16(d_buf)) return fail(PG_ERR_INVALID_ARG, "d_buf is not 16-byte aligned");
-  int64_t T, n_resp, n_qt, n_kvt;
-  pg_status st = check_groups(g, &T, &n_resp, &n_qt, &n_kvt);
+  HostPlan hp;
+  pg_status st = plan_batch(g, hp);
   if (st != PG_OK) return st;
-  Layout L0 = make_layout(T, g->num_groups, n_resp, n_qt, n_kvt);
-  if (buf_bytes < L0.total)
-    return fail(PG_ERR_WORKSPACE, "descriptor buffer too small: need " + std::to_string(L0.total) +
+  const Layout L = layout_of(g, hp);
+  if (buf_bytes < L.total)
+    return fail(PG_ERR_WORKSPACE, "descriptor buffer too small: need " + std::to_string(L.total) +
                                       " bytes, got " + std::to_string(buf_bytes));
-  std::vector<char> host(L0.total);
-  std::vector<int32_t> pos(d_pos_ids ? size_t(T) : 0);
-  Layout L;
+  std::vector<char> host(L.total);
   pg_desc d;
-  st = build_plan(g, host.data(), host.size(), d_pos_ids ? pos.data() : nullptr, &d, &L);
-  if (st != PG_OK) return st;
+  serialize(g, hp, L, host.data(), nullptr, &d);
+  const int64_t T = hp.T;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipMemcpyAsync(d_buf, host.data(), L.total, hipMemcpyHostToDevice, s);
   if (e == hipSuccess && d_pos_ids && T > 0)
-    e = hipMemcpyAsync(d_pos_ids, pos.data(), size_t(T) * 4, hipMemcpyHostToDevice, s);
+    e = hipMemcpyAsync(d_pos_ids, hp.pos.data(), size_t(T) * 4, hipMemcpyHostToDevice, s);
   // the host staging vectors die with this call, so wait for the copies
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) return hip_status(e, "pg_pack copy");
@@ -425,10 +527,15 @@ pg_status pg_attn_fwd(const pg_desc *d, pg_dtype t, float softmax_scale, const v
 }
 
 size_t pg_attn_bwd_workspace_size(const pg_desc *d, pg_dtype t) {
-  (void)t;
   if (check_desc(d) != PG_OK) return 0;
-  // delta and the base-2 logsumexp, float [Hq, T] each
-  return std::max<size_t>(16, 2 * align16(size_t(d->num_q_heads) * size_t(d->total_rows) * 4));
+  // delta and the base-2 logsumexp, float [Hq, T] each; for bf16 also the
+  // float dK/dV partial sums of the split key tiles
+  const size_t rows = align16(size_t(d->num_q_heads) * size_t(d->total_rows) * 4);
+  size_t parts = 0;
+  if (t == PG_BF16)
+    parts = size_t(d->num_kv_parts) * size_t(d->num_kv_heads) * 2 * PG_TILE_KV *
+            size_t(d->head_dim) * 4;
+  return std::max<size_t>(16, 2 * rows + parts);
 }
 
 pg_status pg_attn_bwd(const pg_desc *d, pg_dtype t, float softmax_scale, const void *q,
@@ -442,6 +549,10 @@ pg_status pg_attn_bwd(const pg_desc *d, pg_dtype t, float softmax_scale, const v
   if ((st = check_ptrs({{q, "q"}, {k, "k"}, {v, "v"}, {o, "o"}, {lse, "lse"}, {dout, "dout"},
                         {dq, "dq"}, {dk, "dk"}, {dv, "dv"}, {workspace, "workspace"}})) != PG_OK)
     return st;
+  if (t == PG_BF16 && (size_t(d->total_rows) + 32) * size_t(d->num_q_heads) *
+                             size_t(d->head_dim) * 2 > size_t(INT32_MAX))
+    return fail(PG_ERR_UNSUPPORTED,
+                "bf16 backward: q and dout must each be under 2 GiB (32-bit buffer offsets)");
   const size_t need = pg_attn_bwd_workspace_size(d, t);
   if (ws_bytes < need)
     return fail(PG_ERR_WORKSPACE, "workspace too small: need " + std::to_string(need) +
@@ -450,13 +561,15 @@ pg_status pg_attn_bwd(const pg_desc *d, pg_dtype t, float softmax_scale, const v
   const float scale = resolve_scale(softmax_scale, p.D);
   hipStream_t s = static_cast<hipStream_t>(stream);
   float *delta = static_cast<float *>(workspace);
-  float *lse2 = reinterpret_cast<float *>(static_cast<char *>(workspace) +
-                                          align16(size_t(p.Hq) * size_t(p.T) * 4));
+  const size_t rows = align16(size_t(p.Hq) * size_t(p.T) * 4);
+  float *lse2 = reinterpret_cast<float *>(static_cast<char *>(workspace) + rows);
+  float *partial = reinterpret_cast<float *>(static_cast<char *>(workspace) + 2 * rows);
   hipError_t e = timed(PG_KERNEL_BWD_PRE, s,
                        [&] { return pg::launch_bwd_pre(p, t, o, dout, lse, delta, lse2, s); });
   if (e != hipSuccess) return hip_status(e, "pg_attn_bwd preprocess launch");
   e = timed(PG_KERNEL_BWD_DKDV, s, [&] {
-    return (t == PG_BF16) ? pg::launch_bwd_dkdv_bf16(p, scale, q, k, v, lse2, delta, dout, dk, dv, s)
+    return (t == PG_BF16) ? pg::launch_bwd_dkdv_bf16(p, scale, q, k, v, lse2, delta, dout, dk, dv,
+                                                     partial, s)
                           : pg::launch_bwd_dkdv_f32(p, scale, q, k, v, lse2, delta, dout, dk, dv, s);
   });
   if (e == hipSuccess)

@@ -9,10 +9,14 @@
 // the G prefix copies.  No floating-point atomics are used:
 //   * dkdv: key-stationary.  A workgroup owns 128 key rows of one key/value
 //     head and walks, in a fixed order, every query head of that kv head and
-//     every 64-row query chunk in [k0, q_end), accumulating dK^T and dV^T in
-//     registers (split over two waves per 32-key group, see below).  For a prefix tile that walk covers the prefix rows and all
-//     responses of the group, so the group reduction of Lemma 2.1 happens in
-//     registers, in a fixed order.
+//     every 32-row query block of its range, accumulating dK^T and dV^T in
+//     registers (split over two waves per 32-key group, see below).  For a
+//     prefix tile that walk covers the prefix rows and all responses of the
+//     group, so the group reduction of Lemma 2.1 happens in registers, in a
+//     fixed order.  When that walk alone outweighs the mean work per compute
+//     unit (a short prefix shared by many responses), the planner cuts it
+//     into pieces of whole query blocks: each piece writes float partial sums
+//     and dkdv_sum_kernel adds them in piece order.
 //   * dq: query-stationary, over the same two key segments as the forward.
 // Both are deterministic: every output element is written by exactly one
 // lane, after a reduction whose order does not depend on scheduling.
@@ -79,11 +83,11 @@ struct DkdvCfg {
 
 template <int D>
 __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
-    const int32_t *__restrict__ kv_tiles, const int32_t *__restrict__ row_hi,
+    const int32_t *__restrict__ kv_items, const int32_t *__restrict__ row_hi,
     const bf16 *__restrict__ Q, const bf16 *__restrict__ K, const bf16 *__restrict__ V,
     const float *__restrict__ LSE2, const float *__restrict__ Delta, const bf16 *__restrict__ dO,
-    bf16 *__restrict__ dK, bf16 *__restrict__ dV, int T, int Hq, int Hkv, float scale_log2,
-    float scale) {
+    bf16 *__restrict__ dK, bf16 *__restrict__ dV, float *__restrict__ partial, int T, int Hq,
+    int Hkv, float scale_log2, float scale) {
   using C = DkdvCfg<D>;
   // Q and dO rows of a step, row-major and swizzled: read as MFMA rows for
   // S = Q K^T and dP = dO V^T, and transposed for dV^T += dO^T P and
@@ -96,11 +100,13 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
   // layout: [group][parity][register quad][lane].
   __shared__ __attribute__((aligned(16))) f32x4 sP[C::NG][2][4][64];
 
-  int tile, hk;
-  xcd_kvhead_work(blockIdx.x, Hkv, tile, hk);
+  int item, hk;
+  xcd_kvhead_work(blockIdx.x, Hkv, item, hk);
   const int rep = Hq / Hkv;
-  const int k0 = kv_tiles[4 * tile + 0], k1 = kv_tiles[4 * tile + 1];
-  const int qend = kv_tiles[4 * tile + 2];
+  // key rows [k0, k1), query rows [qa, qb); part >= 0: one piece of a cut tile
+  const int k0 = kv_items[8 * item + 0], k1 = kv_items[8 * item + 1];
+  const int qa = kv_items[8 * item + 2], qb = kv_items[8 * item + 3];
+  const int part = kv_items[8 * item + 4];
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int l32 = lane & 31, hi = lane >> 5;
   const bool roleA = wave < C::NG;        // S, P, dV   (else dP, dS, dK)
@@ -125,24 +131,24 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
   frag.init(lane);
 
   // K (role A) or V (role B) rows of the group as MFMA B operands:
-  // column = key l32, k = d.
+  // column = key l32, k = d.  The resource spans rows [kw0, k1), so keys
+  // past the tile read as zero; the head offset rides in the scalar offset.
   bf16x8 kvf[D / 16];
   {
-    const bf16 *src = (roleA ? K : V) + ((size_t)key * Hkv + hk) * D + 8 * hi;
+    const size_t kv_row = (size_t)Hkv * D * sizeof(bf16);
+    const __amdgpu_buffer_rsrc_t rKV = buffer_resource(
+        (roleA ? K : V) + (size_t)kw0 * Hkv * D, group_active ? (size_t)(k1 - kw0) * kv_row : 0);
+    const int voff = l32 * (int)kv_row + 16 * hi;
 #pragma unroll
-    for (int st = 0; st < D / 16; ++st) {
-      if (key_ok) {
-        kvf[st] = *reinterpret_cast<const bf16x8 *>(src + 16 * st);
-      } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) kvf[st][j] = (__bf16)0.f;
-      }
-    }
+    for (int st = 0; st < D / 16; ++st)
+      kvf[st] = __builtin_bit_cast(
+          bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rKV, voff + 32 * st, hk * D * 2, 0));
   }
   // Let these loads complete here: left to the compiler, the wait for them
   // lands at their first use inside the step loop, where it would also wait
   // for the prefetch copies issued in the same step.
   wait_async_loads();
+  pin(kvf);
 
   // dV^T (role A) or dK^T (role B): register r of lane l holds
   // d = 32 nb + mfma_row(r, hi), key = l32.
@@ -152,18 +158,18 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[nb][r] = 0.f;
 
-  // Steps: 32-row query blocks [k0 + 32 b, ...) for b = nB-1 down to 0, the
+  // Steps: 32-row query blocks [qa + 32 b, ...) for b = nB-1 down to 0, the
   // query heads of the kv head interleaved per block.  Walking down from
   // the end of the group, which every prefix tile of the group shares, keeps
   // the workgroups that run side by side on one XCD on the same Q/dO rows,
   // so those rows are fetched into that XCD's L2 once.
-  const int nB = (qend - k0 + C::BM - 1) / C::BM;  // blocks per query head
+  const int nB = (qb - qa + C::BM - 1) / C::BM;  // blocks per query head
   const int nS = nB * rep;
   const size_t q_row = (size_t)Hq * D;
   auto step_of = [&](int n, int &h, int &c0) {
     const int bi = n / rep;
     h = hk * rep + (n - bi * rep);
-    c0 = k0 + (nB - 1 - bi) * C::BM;
+    c0 = qa + (nB - 1 - bi) * C::BM;
   };
 
   // Copies of step n into slot n % NSLOT go through registers: every thread
@@ -178,10 +184,11 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
   const bool chunk_owner = tid < C::BM * CPR;
   const int crow = tid / CPR, cch = tid % CPR;
   const int cdst = crow * D + ((cch ^ swz_chunk<D>(crow)) << 3);  // swizzled, elements
-  // Buffer resources over Q, dO, LSE2 and delta: a load is then a scalar
-  // descriptor + a scalar per-step offset + the thread's fixed byte offset,
-  // so it holds no per-step vector address registers, and rows past the end
-  // of a tensor read as zero (the visibility mask covers them).
+  // Buffer loads with one scalar descriptor per tensor: the row offset of
+  // the step is part of the vector offset, which the range check covers, so
+  // rows past the end of the batch read as zero (the visibility mask covers
+  // them); the head offset rides in the unchecked scalar offset and stays
+  // inside the row.
   const __amdgpu_buffer_rsrc_t rQ = buffer_resource(Q, (size_t)T * q_row * sizeof(bf16));
   const __amdgpu_buffer_rsrc_t rdO = buffer_resource(dO, (size_t)T * q_row * sizeof(bf16));
   const __amdgpu_buffer_rsrc_t rL = buffer_resource(wave == 0 ? LSE2 : Delta, (size_t)Hq * T * 4);
@@ -192,13 +199,15 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
     int h, c0;
     step_of(n, h, c0);
     if (chunk_owner) {
-      const int soff = (int)(((size_t)c0 * q_row + (size_t)h * D) * sizeof(bf16));
-      stq = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rQ, coff, soff, 0));
-      sto = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rdO, coff, soff, 0));
+      const int off = coff + c0 * (int)(q_row * sizeof(bf16));
+      stq = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rQ, off, h * D * 2, 0));
+      sto = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rdO, off, h * D * 2, 0));
     }
-    if (wave < 2 && lane < C::BM)
-      stl = __builtin_bit_cast(
-          float, __builtin_amdgcn_raw_buffer_load_b32(rL, lane * 4, (int)(((size_t)h * T + c0) * 4), 0));
+    if (wave < 2 && lane < C::BM) {
+      // rows past the batch: an offset past the resource, read as zero
+      const int off = (c0 + lane < T) ? (h * T + c0 + lane) * 4 : 0x7fffffff;
+      stl = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rL, off, 0, 0));
+    }
   };
   auto commit = [&](int n) {
     const int slot = n % C::NSLOT;
@@ -230,7 +239,11 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
   }
   // Drain the prologue's loads here: otherwise the compiler's wait analysis
   // carries them into the loop and waits for every step's own loads mid-step.
+  // (pin keeps the loads above the wait: the wait itself orders no memory.)
   wait_async_loads();
+  pin(stq);
+  pin(sto);
+  pin(stl);
   if (roleA) {
     // S -> P for step n; P (fp32) goes to LDS for wave B (which uses it in
     // step n+1) and, packed to bf16, into dV^T += dO_n^T P_n right away.
@@ -274,6 +287,11 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
       }
     }
   } else {
+    // Nothing is in flight here, but the compiler lays the role-A loop out
+    // with a path into this one, and its wait analysis would otherwise carry
+    // that loop's copies in and wait for them (and so for this step's own
+    // copies) in the middle of every step.
+    wait_async_loads();
     f32x16 dp;  // dP of the previous step
     bool live_prev = false;
     for (int n = 0; n <= nS; ++n) {
@@ -314,17 +332,65 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
   }
 
   if (!group_active || !key_ok) return;
-  bf16 *dst = (roleA ? dV : dK) + ((size_t)key * Hkv + hk) * D;
   const float f = roleA ? 1.f : scale;
+  if (part < 0) {
+    bf16 *dst = (roleA ? dV : dK) + ((size_t)key * Hkv + hk) * D;
 #pragma unroll
-  for (int nb = 0; nb < D / 32; ++nb)
+    for (int nb = 0; nb < D / 32; ++nb)
 #pragma unroll
-    for (int rq = 0; rq < 4; ++rq) {
-      const int d0 = nb * 32 + rq * 8 + hi * 4;
-      *reinterpret_cast<u32x2 *>(dst + d0) =
-          pack4_bf16(acc[nb][rq * 4 + 0] * f, acc[nb][rq * 4 + 1] * f, acc[nb][rq * 4 + 2] * f,
-                     acc[nb][rq * 4 + 3] * f);
+      for (int rq = 0; rq < 4; ++rq) {
+        const int d0 = nb * 32 + rq * 8 + hi * 4;
+        *reinterpret_cast<u32x2 *>(dst + d0) =
+            pack4_bf16(acc[nb][rq * 4 + 0] * f, acc[nb][rq * 4 + 1] * f,
+                       acc[nb][rq * 4 + 2] * f, acc[nb][rq * 4 + 3] * f);
+      }
+  } else {
+    // partial slot [part][hk][dV, dK][key - k0][d], float
+    float *dst = partial + (((size_t)part * Hkv + hk) * 2 + (roleA ? 0 : 1)) * (C::BN * D) +
+                 (size_t)(key - k0) * D;
+#pragma unroll
+    for (int nb = 0; nb < D / 32; ++nb)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const int d0 = nb * 32 + rq * 8 + hi * 4;
+        f32x4 v;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = acc[nb][rq * 4 + j] * f;
+        *reinterpret_cast<f32x4 *>(dst + d0) = v;
+      }
+  }
+}
+
+// Sum of the pieces of each cut key tile, in piece order, to bf16 dK / dV.
+// Block (s, hk, kind): kv_sums[s] = {k0, k1, first part, parts}; kind 0 is
+// dV, 1 is dK.  Each thread adds one 4-float chunk of a key row over the
+// parts.
+template <int D>
+__global__ __launch_bounds__(256) void dkdv_sum_kernel(const int32_t *__restrict__ kv_sums,
+                                                       const float *__restrict__ partial,
+                                                       bf16 *__restrict__ dK,
+                                                       bf16 *__restrict__ dV, int Hkv) {
+  constexpr int BN = PG_TILE_KV, CH = D / 4;
+  const int kind = blockIdx.x & 1;
+  const int sh = blockIdx.x >> 1;
+  const int si = sh / Hkv, hk = sh - si * Hkv;
+  const int k0 = kv_sums[4 * si + 0], k1 = kv_sums[4 * si + 1];
+  const int first = kv_sums[4 * si + 2], np = kv_sums[4 * si + 3];
+  const size_t pstride = (size_t)Hkv * 2 * BN * D;
+  const float *base = partial + (((size_t)first * Hkv + hk) * 2 + kind) * (BN * D);
+  bf16 *out = kind == 0 ? dV : dK;
+  for (int i = threadIdx.x; i < (k1 - k0) * CH; i += 256) {
+    const int kl = i / CH, c = i - kl * CH;
+    const float *src = base + (size_t)kl * D + 4 * c;
+    f32x4 a = *reinterpret_cast<const f32x4 *>(src);
+    for (int j = 1; j < np; ++j) {
+      const f32x4 b = *reinterpret_cast<const f32x4 *>(src + j * pstride);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a[e] += b[e];
     }
+    *reinterpret_cast<u32x2 *>(out + ((size_t)(k0 + kl) * Hkv + hk) * D + 4 * c) =
+        pack4_bf16(a[0], a[1], a[2], a[3]);
+  }
 }
 
 // ---------------------------------------------------------------- dQ
@@ -515,18 +581,30 @@ hipError_t launch_bwd_pre(const Plan &p, pg_dtype t, const void *o, const void *
 
 hipError_t launch_bwd_dkdv_bf16(const Plan &p, float scale, const void *q, const void *k,
                                 const void *v, const float *lse, const float *delta,
-                                const void *dout, void *dk, void *dv, hipStream_t s) {
-  if (p.n_kv_tiles == 0) return hipSuccess;
-  const dim3 grid((unsigned)p.n_kv_tiles * (unsigned)p.Hkv), block(DkdvCfg<128>::NT);
+                                const void *dout, void *dk, void *dv, float *partial,
+                                hipStream_t s) {
+  if (p.n_kv_items == 0) return hipSuccess;
+  const dim3 grid((unsigned)p.n_kv_items * (unsigned)p.Hkv), block(DkdvCfg<128>::NT);
   const float sl2 = scale * kLog2e;
   if (p.D == 128)
-    hipLaunchKernelGGL(dkdv_bf16_kernel<128>, grid, block, 0, s, p.kv_tiles, p.row_hi,
+    hipLaunchKernelGGL(dkdv_bf16_kernel<128>, grid, block, 0, s, p.kv_items, p.row_hi,
                        (const bf16 *)q, (const bf16 *)k, (const bf16 *)v, lse, delta,
-                       (const bf16 *)dout, (bf16 *)dk, (bf16 *)dv, p.T, p.Hq, p.Hkv, sl2, scale);
+                       (const bf16 *)dout, (bf16 *)dk, (bf16 *)dv, partial, p.T, p.Hq, p.Hkv,
+                       sl2, scale);
   else
-    hipLaunchKernelGGL(dkdv_bf16_kernel<64>, grid, block, 0, s, p.kv_tiles, p.row_hi,
+    hipLaunchKernelGGL(dkdv_bf16_kernel<64>, grid, block, 0, s, p.kv_items, p.row_hi,
                        (const bf16 *)q, (const bf16 *)k, (const bf16 *)v, lse, delta,
-                       (const bf16 *)dout, (bf16 *)dk, (bf16 *)dv, p.T, p.Hq, p.Hkv, sl2, scale);
+                       (const bf16 *)dout, (bf16 *)dk, (bf16 *)dv, partial, p.T, p.Hq, p.Hkv,
+                       sl2, scale);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.n_kv_sums == 0) return e;
+  const dim3 sgrid((unsigned)p.n_kv_sums * (unsigned)p.Hkv * 2u), sblock(256);
+  if (p.D == 128)
+    hipLaunchKernelGGL(dkdv_sum_kernel<128>, sgrid, sblock, 0, s, p.kv_sums,
+                       (const float *)partial, (bf16 *)dk, (bf16 *)dv, p.Hkv);
+  else
+    hipLaunchKernelGGL(dkdv_sum_kernel<64>, sgrid, sblock, 0, s, p.kv_sums,
+                       (const float *)partial, (bf16 *)dk, (bf16 *)dv, p.Hkv);
   return hipGetLastError();
 }
 

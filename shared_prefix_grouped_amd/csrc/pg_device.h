@@ -259,11 +259,29 @@ __device__ __forceinline__ void xcd_kvhead_work(int bid, int Hkv, int &tile, int
   }
 }
 
-// Raw buffer resource (stride 0) over `bytes` bytes at `p`, for buffer loads
-// with a scalar descriptor: accesses at or past `bytes` return zero.  Word 3
-// is the gfx9-family raw-buffer format (32-bit data, no swizzle).
+// Raw buffer resource (stride 0) over `bytes` (< 2^32) bytes at `p`, for
+// buffer loads with a scalar descriptor.  The range check covers the vector
+// offset plus the instruction offset only: a load whose vector + immediate
+// offset is at or past `bytes` returns zero and reads nothing, while the
+// scalar offset is added unchecked, so it must keep every in-range access
+// inside the tensor by itself.  Word 3 is the gfx9-family raw-buffer format
+// (32-bit data, no swizzle).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_resource(const void *p, size_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0,
+                                           (int)(uint32_t)bytes, 0x00020000);
+}
+
+// An empty asm that claims to read and rewrite x: a load into x is complete
+// before it (the wait is inserted there), so the load cannot sink below a
+// preceding s_waitcnt, and no use of x moves above it.
+template <typename Tv>
+__device__ __forceinline__ void pin(Tv &x) {
+  asm volatile("" : "+v"(x));
+}
+template <typename Tv, int N>
+__device__ __forceinline__ void pin(Tv (&x)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) pin(x[i]);
 }
 
 typedef __attribute__((address_space(1))) const char gbl_cchar;

@@ -13,8 +13,10 @@ namespace pg {
 struct Plan {
   int T, Hq, Hkv, D;
   int n_q_tiles, n_kv_tiles;
+  int n_kv_items, n_kv_sums, n_kv_parts;
   const int32_t *row_lo, *row_hi;
   const int32_t *q_tiles, *kv_tiles;
+  const int32_t *kv_items, *kv_sums;
 };
 
 // log2(e): scores are kept in the base-2 domain inside the kernels so that the
@@ -33,10 +35,13 @@ hipError_t launch_fwd_f32(const Plan &p, float scale, const void *q, const void 
 hipError_t launch_bwd_pre(const Plan &p, pg_dtype t, const void *o, const void *dout,
                           const float *lse, float *delta, float *lse2, hipStream_t s);
 // dK, dV (key-stationary) and dQ (query-stationary); no atomics.  `lse`
-// here is the base-2 logsumexp written by the preprocess.
+// here is the base-2 logsumexp written by the preprocess.  The bf16 dK/dV
+// launch walks the plan's kv_items; `partial` holds n_kv_parts float slots of
+// [Hkv][2][PG_TILE_KV][D] for the pieces of split key tiles.
 hipError_t launch_bwd_dkdv_bf16(const Plan &p, float scale, const void *q, const void *k,
                                 const void *v, const float *lse, const float *delta,
-                                const void *dout, void *dk, void *dv, hipStream_t s);
+                                const void *dout, void *dk, void *dv, float *partial,
+                                hipStream_t s);
 hipError_t launch_bwd_dq_bf16(const Plan &p, float scale, const void *q, const void *k,
                               const void *v, const float *lse, const float *delta,
                               const void *dout, void *dq, hipStream_t s);

@@ -102,6 +102,64 @@ def test_planner_random_layouts():
             costs.append(int(vis[:, k0:k1].sum()))
         assert np.all(covered == 1)
         assert costs == sorted(costs, reverse=True)
+        _check_kv_items(plan, vis, rep=4)
+
+
+def _check_kv_items(plan, vis, rep):
+    """The dK/dV work list covers every visible (query, key) pair exactly once.
+
+    Uncut key tiles appear whole; a cut tile's pieces split [k0, q_end) at
+    32-row query blocks, number their float partial slots consecutively in
+    query order, each hold at least 32 (query head, block) steps, and are
+    listed in kv_sums; the list is ordered by decreasing cost."""
+    items, sums = plan["kv_items"], plan["kv_sums"]
+    tiles = {(int(k0), int(k1)): int(qend) for k0, k1, qend, _ in plan["kv_tiles"]}
+    assert np.all(items[:, 5:] == 0)
+    by_tile = {}
+    costs = []
+    for k0, k1, qa, qb, part, *_ in items.tolist():
+        assert (k0, k1) in tiles and k0 <= qa < qb <= tiles[(k0, k1)]
+        by_tile.setdefault((k0, k1), []).append((qa, qb, part))
+        costs.append(int(vis[qa:qb, k0:k1].sum()))
+    assert costs == sorted(costs, reverse=True)
+    assert sum(costs) == plan["pairs"]
+    assert set(by_tile) == set(tiles)
+    cut = {(int(k0), int(k1)): (int(first), int(n)) for k0, k1, first, n in sums}
+    used = []
+    for key, pieces in by_tile.items():
+        k0, qend = key[0], tiles[key]
+        pieces.sort()
+        if key not in cut:
+            assert pieces == [(k0, qend, -1)]
+            continue
+        first, n = cut[key]
+        assert n >= 2 and len(pieces) == n
+        assert [pc[2] for pc in pieces] == list(range(first, first + n))
+        assert pieces[0][0] == k0 and pieces[-1][1] == qend
+        for (qa, qb, _), nxt in zip(pieces, pieces[1:] + [None]):
+            assert (qa - k0) % 32 == 0
+            assert -(-(qb - qa) // 32) * rep >= 32
+            if nxt is not None:
+                assert nxt[0] == qb
+        used += [pc[2] for pc in pieces]
+    assert sorted(used) == list(range(plan["num_kv_parts"]))
+
+
+def test_short_prefix_tiles_are_cut_and_long_ones_are_not():
+    """A 40-row prefix shared by 24 responses holds most of the dK/dV work in
+    one key tile: it is cut.  At the headline shape (8192-row prefix, 16
+    responses) every tile is under the per-unit mean and stays whole."""
+    groups = [(40, [97] * 24)]
+    plan = pg.pg_pack_host(groups, 8, 2, 128)
+    _, T = member_sequences(groups)
+    vis = _visibility_from_plan(plan)
+    assert len(plan["kv_sums"]) == 1 and plan["kv_sums"][0, :2].tolist() == [0, 128]
+    _check_kv_items(plan, vis, rep=4)
+    from workloads import attention_workloads
+    w = attention_workloads()["bf16_gqa_g16_p8192"]
+    plan = pg.pg_pack_host([(g.prefix_len, list(g.resp_lens)) for g in w.groups],
+                           w.num_q_heads, w.num_kv_heads, w.head_dim)
+    assert plan["num_kv_parts"] == 0 and len(plan["kv_items"]) == plan["num_kv_tiles"]
 
 
 def test_full_size_layouts_plan():
@@ -192,7 +250,15 @@ def test_fwd_bwd_validate_before_launch():
     assert L.pg_attn_fwd(ctypes.byref(desc), pg.PG_BF16, f, p, bad, p, p, p, None) == pg.PG_ERR_INVALID_ARG
     assert "aligned" in L.pg_last_error().decode()
     ws = L.pg_attn_bwd_workspace_size(ctypes.byref(desc), pg.PG_BF16)
-    assert ws >= desc.num_q_heads * desc.total_rows * 4
+    rows = -(-desc.num_q_heads * desc.total_rows * 4 // 16) * 16
+    assert ws == max(16, 2 * rows + desc.num_kv_parts * desc.num_kv_heads * 2 * pg.PG_TILE_KV
+                     * desc.head_dim * 4)
+    assert L.pg_attn_bwd_workspace_size(ctypes.byref(desc), pg.PG_F32) == max(16, 2 * rows)
+    cut, _cbuf = _host_desc(((40, [97] * 24),), 8, 2, 128)  # one cut prefix tile
+    assert cut.num_kv_parts >= 2
+    rows_c = -(-8 * cut.total_rows * 4 // 16) * 16
+    assert (L.pg_attn_bwd_workspace_size(ctypes.byref(cut), pg.PG_BF16)
+            == 2 * rows_c + cut.num_kv_parts * 2 * 2 * pg.PG_TILE_KV * 128 * 4)
     args = [p] * 10
     st = L.pg_attn_bwd(ctypes.byref(desc), pg.PG_BF16, f, *args, ws - 1, None)
     assert st == pg.PG_ERR_WORKSPACE

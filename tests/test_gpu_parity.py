@@ -73,6 +73,11 @@ SMALL = [
     ("many_short", [(65, [3] * 40)], 2, 2, 64),
     ("empty_prefix_only_resp", [(0, [257])], 2, 2, 128),
     ("prefix_only", [(333, [0, 0])], 4, 4, 64),
+    # short prefix shared by many responses: the prefix key tiles are cut into
+    # pieces whose float partial sums are added by a second kernel
+    ("short_prefix_g24", [(40, [97] * 24)], 8, 2, 128),
+    ("short_prefix_2groups_d64", [(150, [61] * 20 + [3, 200]), (7, [33] * 12)], 4, 2, 64),
+    ("short_prefix_mha", [(130, [50] * 40)], 2, 2, 128),
 ]
 
 
@@ -207,6 +212,7 @@ def test_bf16_varlen_2groups_full_size_sampled():
 
 @pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("f32", 128), ("f32", 64)])
 def test_deterministic_bitwise(dtype, d):
+    # both groups' prefix key tiles are cut for bf16 (partial sums + second kernel)
     w = scaled_down("det", [(1000, [333, 12, 700]), (64, [500])], dtype, 8, 2, d, seed=5)
     groups = _groups_of(w)
     arrs = draw_attention_inputs(w)
