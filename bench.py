@@ -2,6 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--no-baseline] [--no-cpu] [--cpu-seconds S] [--forward-only]
+                    [--ratio-sweep] [--pack-rows]
 
 One step is one pass of the whole path over one packed batch with inputs
 already resident in HBM: pg_pack (plan + descriptor upload), pg_attn_fwd and
@@ -13,6 +14,9 @@ pg_attn_bwd.  Prints ONE JSON line on stdout; progress goes to stderr.
            repeated-prefix layout (same kernels), their ratio beside the exact
            attention-FLOP ratio pairs_g / pairs_b and its limit 1/G, and the
            bytes of the path's tensors in each layout.  One JSON line.
+--pack-rows  pg_pack_rows gathering the workload's [T, Hq, d] bf16 rows from a
+           prefix buffer and a response buffer into packed order; value in
+           GB/s (read + write) against 8 TB/s of HBM.  One JSON line.
 --forward-only  scoring mode: a step is pg_pack + pg_attn_fwd without the
            logsumexp store (many short responses scored against one long
            context; default workload bf16_scoring_p32768); value is then
@@ -70,6 +74,8 @@ def parse(argv=None):
                     help="time grouped vs repeated-prefix layouts over prefix/response ratios")
     ap.add_argument("--forward-only", action="store_true",
                     help="score without backward and without storing the logsumexp")
+    ap.add_argument("--pack-rows", action="store_true",
+                    help="time pg_pack_rows gathering the workload's [T, Hq, d] rows into packed order")
     ap.add_argument("--no-baseline", action="store_true", help="skip the repeated-prefix run")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -248,6 +254,43 @@ def ratio_sweep(a, pg, torch) -> dict:
             "points": points}
 
 
+def pack_rows_bench(a, pg, torch, w) -> dict:
+    """pg_pack_rows on the workload's layout with [*, Hq, d] rows: a pure copy,
+    so the roofline is HBM bandwidth over 2 * T * row bytes per call."""
+    groups = groups_of(w)
+    batch = pg.pg_pack(groups, w.num_q_heads, w.num_kv_heads, w.head_dim)
+    n_pre = batch.desc.total_prefix_rows
+    T = batch.total_rows
+    tail = (w.num_q_heads, w.head_dim)
+    gen = torch.Generator(device="cuda").manual_seed(8)
+    pre = torch.randn((n_pre,) + tail, generator=gen, device="cuda").to(torch.bfloat16)
+    resp = torch.randn((T - n_pre,) + tail, generator=gen, device="cuda").to(torch.bfloat16)
+    out = torch.empty((T,) + tail, dtype=torch.bfloat16, device="cuda")
+    for _ in range(a.warmup):
+        pg.pg_pack_rows(batch, pre, resp, out=out)
+    torch.cuda.synchronize()
+    pg.pg_kernel_timing(True)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(a.steps):
+        pg.pg_pack_rows(batch, pre, resp, out=out)
+    stop.record()
+    torch.cuda.synchronize()
+    n, kms = pg.pg_kernel_times()["rows"]
+    pg.pg_kernel_timing(False)
+    ms = start.elapsed_time(stop) / a.steps
+    moved = 2 * T * out[0].numel() * out.element_size()
+    gbs = moved / (kms / n * 1e-3) / 1e9
+    log(f"[bench] pack_rows: {ms:.4f} ms per call, kernel {kms / n:.4f} ms, {gbs:.0f} GB/s")
+    return {"metric": "packed-row gather GB/s (pg_pack_rows)", "value": round(gbs, 1), "unit": "GB/s",
+            "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms, 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic (seeded N(0,1) rows)",
+            "config": {"workload": w.name, "row_shape": list(tail), "rows": T, "prefix_rows": n_pre},
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": 8000.0, "unit": "GB/s",
+                         "frac": round(gbs / 8000.0, 4), "traffic": None}}
+
+
 def main(argv=None) -> int:
     a = parse(argv)
     if a.gpus != 1:
@@ -267,6 +310,9 @@ def main(argv=None) -> int:
         return 0
     fwd_only = a.forward_only
     w = attention_workloads()[a.workload or ("bf16_scoring_p32768" if fwd_only else "bf16_gqa_g16_p8192")]
+    if a.pack_rows:
+        print(json.dumps(pack_rows_bench(a, pg, torch, w)), flush=True)
+        return 0
     groups = groups_of(w)
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     log(f"[bench] workload {w.name}: {w.description}; T={w.total_rows}")

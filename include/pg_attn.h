@@ -126,6 +126,9 @@ typedef struct {
  *   group_start  [num_groups + 1], prefix_end [num_groups],
  *   resp_start   [num_resp], resp_len [num_resp], resp_group [num_resp]:
  *                the packed offsets, for callers.
+ *   prefix_before [num_groups + 1]: prefix rows of the groups before g
+ *                (prefix_before[num_groups] = total_prefix_rows), the
+ *                offsets of pg_pack_rows' prefix buffer.
  *   pairs           unmasked (query, key) pairs per query head;
  *   baseline_pairs  the same count for the repeated-prefix layout (each
  *                   [P; R_i] on its own). */
@@ -134,6 +137,7 @@ typedef struct {
   int32_t num_q_heads, num_kv_heads, head_dim;
   int32_t num_q_tiles, num_kv_tiles;
   int32_t num_kv_items, num_kv_sums, num_kv_parts;
+  int32_t total_prefix_rows;
   int64_t pairs, baseline_pairs;
   const int32_t *row_lo;
   const int32_t *row_hi;
@@ -143,6 +147,7 @@ typedef struct {
   const int32_t *kv_sums;
   const int32_t *group_start;
   const int32_t *prefix_end;
+  const int32_t *prefix_before;
   const int32_t *resp_start;
   const int32_t *resp_len;
   const int32_t *resp_group;
@@ -168,6 +173,26 @@ pg_status pg_pack(const pg_groups *g, void *d_buf, size_t buf_bytes, int32_t *d_
  * pointers in *out address `h_buf`.  For inspection and tests. */
 pg_status pg_pack_host(const pg_groups *g, void *h_buf, size_t buf_bytes, int32_t *h_pos_ids,
                        pg_desc *out);
+
+/* Gather per-row data into the packed layout: the shared prefix of each group
+ * once, then its responses back to back (skillsmp.com "prefix-grouper-grpo",
+ * "Step 3: Restructure Input Format", without the padding rows).  prefix_rows
+ * holds the groups' prefix rows one group after another [total_prefix_rows],
+ * resp_rows every response's rows in pg_groups order [T - total_prefix_rows],
+ * packed_rows receives [T]; each row is row_bytes bytes (a positive multiple
+ * of 4; 16-byte chunks and 16-byte aligned pointers when it is a multiple of
+ * 16, else 4-byte).  Token ids, hidden states or any [T, ...] tensor of the
+ * batch.  Device buffers, caller-owned, not overlapping; a buffer with no
+ * rows may be NULL.  Enqueued on `stream`; one kernel reading and writing
+ * each byte once. */
+pg_status pg_pack_rows(const pg_desc *d, const void *prefix_rows, const void *resp_rows,
+                       void *packed_rows, size_t row_bytes, void *stream);
+
+/* The inverse scatter: packed rows back to the prefix and response buffers
+ * (same layouts and rules as pg_pack_rows), e.g. to read the response rows of
+ * an output or a gradient per response. */
+pg_status pg_unpack_rows(const pg_desc *d, const void *packed_rows, void *prefix_rows,
+                         void *resp_rows, size_t row_bytes, void *stream);
 
 /* Forward: O = grouped attention(Q, K, V) and LSE, for every packed row and
  * query head.  softmax_scale <= 0 selects 1/sqrt(head_dim).  Prefix rows are
@@ -226,7 +251,8 @@ pg_status pg_rope(const pg_desc *d, pg_dtype t, void *x, int32_t num_heads, int3
 #define PG_KERNEL_BWD_DKDV 2
 #define PG_KERNEL_BWD_DQ 3
 #define PG_KERNEL_ROPE 4
-#define PG_KERNEL_COUNT 5
+#define PG_KERNEL_ROWS 5
+#define PG_KERNEL_COUNT 6
 pg_status pg_kernel_timing(int32_t enable);
 pg_status pg_kernel_times(int32_t kernel_id, int64_t *launches, double *total_ms);
 const char *pg_kernel_name(int32_t kernel_id);

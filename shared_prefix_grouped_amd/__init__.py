@@ -35,9 +35,10 @@ PG_TILE_Q = 128
 PG_TILE_KV = 128
 
 EXPORTED = ("pg_pack_buffer_size", "pg_pack", "pg_pack_host", "pg_attn_fwd",
-            "pg_attn_bwd_workspace_size", "pg_attn_bwd", "pg_rope", "pg_kernel_timing",
+            "pg_attn_bwd_workspace_size", "pg_attn_bwd", "pg_rope", "pg_pack_rows",
+            "pg_unpack_rows", "pg_kernel_timing",
             "pg_kernel_times", "pg_kernel_name", "pg_last_error", "pg_version")
-KERNELS = ("fwd", "bwd_pre", "bwd_dkdv", "bwd_dq", "rope")
+KERNELS = ("fwd", "bwd_pre", "bwd_dkdv", "bwd_dq", "rope", "rows")
 
 
 class LibraryNotBuilt(RuntimeError):
@@ -65,11 +66,12 @@ class PgDesc(ctypes.Structure):
                 ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("num_q_tiles", ctypes.c_int32), ("num_kv_tiles", ctypes.c_int32),
                 ("num_kv_items", ctypes.c_int32), ("num_kv_sums", ctypes.c_int32),
-                ("num_kv_parts", ctypes.c_int32),
+                ("num_kv_parts", ctypes.c_int32), ("total_prefix_rows", ctypes.c_int32),
                 ("pairs", ctypes.c_int64), ("baseline_pairs", ctypes.c_int64),
                 ("row_lo", _i32p), ("row_hi", _i32p), ("q_tiles", _i32p), ("kv_tiles", _i32p),
                 ("kv_items", _i32p), ("kv_sums", _i32p),
-                ("group_start", _i32p), ("prefix_end", _i32p), ("resp_start", _i32p),
+                ("group_start", _i32p), ("prefix_end", _i32p), ("prefix_before", _i32p),
+                ("resp_start", _i32p),
                 ("resp_len", _i32p), ("resp_group", _i32p), ("buf_bytes", ctypes.c_size_t)]
 
 
@@ -101,6 +103,10 @@ def lib() -> ctypes.CDLL:
     L.pg_attn_bwd.restype = ctypes.c_int
     L.pg_rope.argtypes = [Dp, ctypes.c_int, vp, i32, i32, vp, f32, i32, vp]
     L.pg_rope.restype = ctypes.c_int
+    L.pg_pack_rows.argtypes = [Dp, vp, vp, vp, sz, vp]
+    L.pg_pack_rows.restype = ctypes.c_int
+    L.pg_unpack_rows.argtypes = [Dp, vp, vp, vp, sz, vp]
+    L.pg_unpack_rows.restype = ctypes.c_int
     L.pg_kernel_timing.argtypes = [i32]
     L.pg_kernel_timing.restype = ctypes.c_int
     L.pg_kernel_times.argtypes = [i32, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_double)]
@@ -211,6 +217,7 @@ def pg_pack_host(groups: Sequence, num_q_heads: int, num_kv_heads: int, head_dim
         "kv_items": arr(d.kv_items, d.num_kv_items, 8), "kv_sums": arr(d.kv_sums, d.num_kv_sums, 4),
         "num_kv_parts": d.num_kv_parts,
         "group_start": arr(d.group_start, d.num_groups + 1), "prefix_end": arr(d.prefix_end, d.num_groups),
+        "prefix_before": arr(d.prefix_before, d.num_groups + 1), "total_prefix_rows": d.total_prefix_rows,
         "resp_start": arr(d.resp_start, d.num_resp), "resp_len": arr(d.resp_len, d.num_resp),
         "resp_group": arr(d.resp_group, d.num_resp), "pos_ids": pos[:T].copy(),
         "buf_bytes": d.buf_bytes,
@@ -299,6 +306,43 @@ def pg_rope(batch: PackedBatch, x, theta: float = 10000.0, inverse: bool = False
                          int(x.shape[2]), _vp(batch.pos_ids), float(theta), int(bool(inverse)),
                          _stream_ptr(x.device)))
     return x
+
+
+def _rows_check(x, rows: int, tail, dtype, name: str) -> None:
+    if x.dim() < 1 or x.shape[0] != rows or tuple(x.shape[1:]) != tuple(tail) or \
+            x.dtype != dtype or not x.is_contiguous():
+        raise PgError(PG_ERR_INVALID_ARG, f"{name} must be contiguous [{rows}, *{tuple(tail)}] {dtype}")
+
+
+def pg_pack_rows(batch: PackedBatch, prefix_rows, resp_rows, out=None):
+    """Packed [T, ...] rows from the groups' prefix rows [sum P, ...] and the
+    responses' rows [sum R, ...] (same trailing shape and dtype)."""
+    torch = _torch()
+    d = batch.desc
+    n_pre, tail, dt = d.total_prefix_rows, tuple(prefix_rows.shape[1:]), prefix_rows.dtype
+    _rows_check(prefix_rows, n_pre, tail, dt, "prefix_rows")
+    _rows_check(resp_rows, d.total_rows - n_pre, tail, dt, "resp_rows")
+    if out is None:
+        out = torch.empty((d.total_rows,) + tail, dtype=dt, device=prefix_rows.device)
+    _rows_check(out, d.total_rows, tail, dt, "out")
+    row_bytes = int(np.prod(tail, dtype=np.int64)) * prefix_rows.element_size()
+    _check(lib().pg_pack_rows(ctypes.byref(d), _vp(prefix_rows), _vp(resp_rows), _vp(out),
+                              row_bytes, _stream_ptr(out.device)))
+    return out
+
+
+def pg_unpack_rows(batch: PackedBatch, packed_rows):
+    """(prefix rows [sum P, ...], response rows [sum R, ...]) of packed [T, ...] rows."""
+    torch = _torch()
+    d = batch.desc
+    n_pre, tail, dt = d.total_prefix_rows, tuple(packed_rows.shape[1:]), packed_rows.dtype
+    _rows_check(packed_rows, d.total_rows, tail, dt, "packed_rows")
+    pre = torch.empty((n_pre,) + tail, dtype=dt, device=packed_rows.device)
+    resp = torch.empty((d.total_rows - n_pre,) + tail, dtype=dt, device=packed_rows.device)
+    row_bytes = int(np.prod(tail, dtype=np.int64)) * packed_rows.element_size()
+    _check(lib().pg_unpack_rows(ctypes.byref(d), _vp(packed_rows), _vp(pre), _vp(resp), row_bytes,
+                                _stream_ptr(packed_rows.device)))
+    return pre, resp
 
 
 def pg_kernel_timing(enable: bool) -> None:

@@ -37,7 +37,7 @@ size_t align16(size_t x) { return (x + 15) & ~size_t(15); }
 // Byte offsets of each array inside the descriptor buffer.
 struct Layout {
   size_t row_lo, row_hi, q_tiles, kv_tiles, kv_items, kv_sums, group_start, prefix_end,
-      resp_start, resp_len, resp_group, total;
+      prefix_before, resp_start, resp_len, resp_group, total;
 };
 
 Layout make_layout(int64_t T, int64_t n_groups, int64_t n_resp, int64_t n_qt, int64_t n_kvt,
@@ -56,6 +56,7 @@ Layout make_layout(int64_t T, int64_t n_groups, int64_t n_resp, int64_t n_qt, in
   take(L.kv_sums, 4 * n_sums);
   take(L.group_start, n_groups + 1);
   take(L.prefix_end, n_groups);
+  take(L.prefix_before, n_groups + 1);
   take(L.resp_start, n_resp);
   take(L.resp_len, n_resp);
   take(L.resp_group, n_resp);
@@ -130,7 +131,7 @@ constexpr int kQueryBlock = 32;
 struct HostPlan {
   int64_t T = 0, n_resp = 0, pairs = 0, base_pairs = 0;
   int32_t n_parts = 0;
-  std::vector<int32_t> row_lo, row_hi, pos, gstart, pend, rstart, rlen, rgroup;
+  std::vector<int32_t> row_lo, row_hi, pos, gstart, pend, pbefore, rstart, rlen, rgroup;
   std::vector<Tile> qt, kvt;
   std::vector<KvItem> items;
   std::vector<int32_t> sums;  // 4 per split tile
@@ -145,6 +146,7 @@ pg_status plan_batch(const pg_groups *g, HostPlan &hp) {
   hp.pos.assign(T, 0);
   hp.gstart.assign(g->num_groups + 1, 0);
   hp.pend.assign(g->num_groups, 0);
+  hp.pbefore.assign(g->num_groups + 1, 0);
   hp.rstart.assign(hp.n_resp, 0);
   hp.rlen.assign(hp.n_resp, 0);
   hp.rgroup.assign(hp.n_resp, 0);
@@ -156,6 +158,7 @@ pg_status plan_batch(const pg_groups *g, HostPlan &hp) {
     const int32_t g0 = t, pe = t + P;
     hp.gstart[gi] = g0;
     hp.pend[gi] = pe;
+    hp.pbefore[gi + 1] = hp.pbefore[gi] + P;
     int32_t gend = pe;
     for (int32_t r = 0; r < g->num_resp[gi]; ++r) gend += g->resp_len[ri + r];
     // prefix rows: own segment is the prefix itself; seen by every later row of the group
@@ -258,6 +261,7 @@ void serialize(const pg_groups *g, const HostPlan &hp, const Layout &L, char *bu
   put(L.kv_sums, hp.sums);
   put(L.group_start, hp.gstart);
   put(L.prefix_end, hp.pend);
+  put(L.prefix_before, hp.pbefore);
   put(L.resp_start, hp.rstart);
   put(L.resp_len, hp.rlen);
   put(L.resp_group, hp.rgroup);
@@ -299,6 +303,7 @@ void serialize(const pg_groups *g, const HostPlan &hp, const Layout &L, char *bu
   d.num_kv_items = int32_t(hp.items.size());
   d.num_kv_sums = int32_t(hp.sums.size() / 4);
   d.num_kv_parts = hp.n_parts;
+  d.total_prefix_rows = hp.pbefore[g->num_groups];
   d.pairs = hp.pairs;
   d.baseline_pairs = hp.base_pairs;
   d.buf_bytes = L.total;
@@ -315,6 +320,7 @@ void point_into(pg_desc *d, const Layout &L, const char *base) {
   d->kv_sums = p(L.kv_sums);
   d->group_start = p(L.group_start);
   d->prefix_end = p(L.prefix_end);
+  d->prefix_before = p(L.prefix_before);
   d->resp_start = p(L.resp_start);
   d->resp_len = p(L.resp_len);
   d->resp_group = p(L.resp_group);
@@ -365,6 +371,10 @@ pg::Plan plan_of(const pg_desc *d) {
   p.n_kv_parts = d->num_kv_parts;
   p.kv_items = d->kv_items;
   p.kv_sums = d->kv_sums;
+  p.n_groups = d->num_groups;
+  p.group_start = d->group_start;
+  p.prefix_end = d->prefix_end;
+  p.prefix_before = d->prefix_before;
   return p;
 }
 
@@ -376,7 +386,8 @@ pg_status hip_status(hipError_t e, const char *what) {
 float resolve_scale(float s, int D) { return s > 0.f ? s : 1.0f / std::sqrt(float(D)); }
 
 // ---------------------------------------------------------------- kernel timing
-const char *const kKernelNames[PG_KERNEL_COUNT] = {"fwd", "bwd_pre", "bwd_dkdv", "bwd_dq", "rope"};
+const char *const kKernelNames[PG_KERNEL_COUNT] = {"fwd",    "bwd_pre", "bwd_dkdv",
+                                                   "bwd_dq", "rope",    "rows"};
 
 struct TimedLaunch {
   int id;
@@ -452,6 +463,46 @@ hipError_t timed(int id, hipStream_t s, F &&launch) {
   t.pending.push_back({id, a, b});
   if (t.pending.size() > 4096) drain(t, false);
   return hipSuccess;
+}
+
+// Shared checks of pg_pack_rows / pg_unpack_rows; the prefix (response)
+// buffer may be NULL when the batch has no prefix (response) rows.
+pg_status check_rows(const pg_desc *d, const void *packed, const void *pre, const void *resp,
+                     size_t row_bytes) {
+  pg_status st = check_desc(d);
+  if (st != PG_OK) return st;
+  if (row_bytes == 0 || row_bytes % 4)
+    return fail(PG_ERR_INVALID_ARG, "row_bytes must be a positive multiple of 4");
+  if (d->num_groups > 0 && (!d->group_start || !d->prefix_end || !d->prefix_before))
+    return fail(PG_ERR_INVALID_ARG, "descriptor arrays are NULL");
+  if (d->total_rows == 0) return PG_OK;
+  if (size_t(d->total_rows) * row_bytes / row_bytes != size_t(d->total_rows) ||
+      size_t(d->total_rows) * row_bytes > (size_t(1) << 46))
+    return fail(PG_ERR_INVALID_ARG, "rows too large");
+  const size_t align = row_bytes % 16 == 0 ? 16 : 4;
+  auto ok = [&](const void *ptr, const char *name, bool needed) -> pg_status {
+    if (!needed) return PG_OK;
+    if (!ptr) return fail(PG_ERR_INVALID_ARG, std::string(name) + " is NULL");
+    if (reinterpret_cast<uintptr_t>(ptr) % align)
+      return fail(PG_ERR_INVALID_ARG, std::string(name) + " is not " + std::to_string(align) +
+                                          "-byte aligned");
+    return PG_OK;
+  };
+  const bool any_prefix = d->total_prefix_rows > 0, any_resp = d->total_rows > d->total_prefix_rows;
+  if ((st = ok(packed, "packed_rows", true)) != PG_OK) return st;
+  if ((st = ok(pre, "prefix_rows", any_prefix)) != PG_OK) return st;
+  return ok(resp, "resp_rows", any_resp);
+}
+
+pg_status rows_call(const pg_desc *d, bool pack, void *packed, void *pre, void *resp,
+                    size_t row_bytes, void *stream) {
+  pg_status st = check_rows(d, packed, pre, resp, row_bytes);
+  if (st != PG_OK || d->total_rows == 0) return st;
+  pg::Plan p = plan_of(d);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return hip_status(timed(PG_KERNEL_ROWS, s,
+                          [&] { return pg::launch_rows(p, pack, packed, pre, resp, row_bytes, s); }),
+                    pack ? "pg_pack_rows launch" : "pg_unpack_rows launch");
 }
 
 }  // namespace
@@ -596,6 +647,18 @@ pg_status pg_rope(const pg_desc *d, pg_dtype t, void *x, int32_t num_heads, int3
                                              theta, inverse, s);
                     }),
                     "pg_rope launch");
+}
+
+pg_status pg_pack_rows(const pg_desc *d, const void *prefix_rows, const void *resp_rows,
+                       void *packed_rows, size_t row_bytes, void *stream) {
+  return rows_call(d, true, packed_rows, const_cast<void *>(prefix_rows),
+                   const_cast<void *>(resp_rows), row_bytes, stream);
+}
+
+pg_status pg_unpack_rows(const pg_desc *d, const void *packed_rows, void *prefix_rows,
+                         void *resp_rows, size_t row_bytes, void *stream) {
+  return rows_call(d, false, const_cast<void *>(packed_rows), prefix_rows, resp_rows, row_bytes,
+                   stream);
 }
 
 pg_status pg_kernel_timing(int32_t enable) {

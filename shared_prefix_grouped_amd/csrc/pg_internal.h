@@ -17,6 +17,8 @@ struct Plan {
   const int32_t *row_lo, *row_hi;
   const int32_t *q_tiles, *kv_tiles;
   const int32_t *kv_items, *kv_sums;
+  int n_groups;
+  const int32_t *group_start, *prefix_end, *prefix_before;
 };
 
 // log2(e): scores are kept in the base-2 domain inside the kernels so that the
@@ -51,6 +53,11 @@ hipError_t launch_bwd_dkdv_f32(const Plan &p, float scale, const void *q, const 
 hipError_t launch_bwd_dq_f32(const Plan &p, float scale, const void *q, const void *k,
                              const void *v, const float *lse, const float *delta,
                              const void *dout, void *dq, hipStream_t s);
+
+// Row gather (pack: the caller's prefix / response row buffers -> packed
+// rows) or scatter (unpack), row_bytes a multiple of 4.
+hipError_t launch_rows(const Plan &p, bool pack, void *packed, void *pre, void *resp,
+                       size_t row_bytes, hipStream_t s);
 
 // Rotary embedding in place.
 hipError_t launch_rope(int T, int H, int D, pg_dtype t, void *x, const int32_t *pos,

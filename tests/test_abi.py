@@ -287,6 +287,38 @@ def test_empty_batch_calls_are_no_ops():
     assert L.pg_attn_bwd(ctypes.byref(desc), pg.PG_BF16, f, *([None] * 10), 0, None) == pg.PG_OK
 
 
+def test_row_gather_plan_and_validation():
+    """prefix_before is the running count of prefix rows; pg_pack_rows /
+    pg_unpack_rows reject bad row sizes, NULL or misaligned buffers on the
+    host, allow NULL for a part with no rows, and do nothing on an empty batch."""
+    groups = [(5, [3, 2]), (0, [4]), (7, [0, 1])]
+    plan = pg.pg_pack_host(groups, 4, 2, 64)
+    assert plan["prefix_before"].tolist() == [0, 5, 5, 12]
+    assert plan["total_prefix_rows"] == 12
+    L = _lib()
+    desc, buf = _host_desc(tuple(groups))
+    p = ctypes.c_void_p(4096)
+    odd = ctypes.c_void_p(4096 + 4)
+    for fn in (L.pg_pack_rows, L.pg_unpack_rows):
+        assert fn(ctypes.byref(desc), p, p, p, 0, None) == pg.PG_ERR_INVALID_ARG
+        assert fn(ctypes.byref(desc), p, p, p, 6, None) == pg.PG_ERR_INVALID_ARG
+        assert "multiple of 4" in L.pg_last_error().decode()
+        assert fn(None, p, p, p, 16, None) == pg.PG_ERR_INVALID_ARG
+    assert L.pg_pack_rows(ctypes.byref(desc), p, p, odd, 16, None) == pg.PG_ERR_INVALID_ARG
+    assert "aligned" in L.pg_last_error().decode()
+    assert L.pg_pack_rows(ctypes.byref(desc), None, p, p, 16, None) == pg.PG_ERR_INVALID_ARG
+    assert "prefix_rows" in L.pg_last_error().decode()
+    assert L.pg_unpack_rows(ctypes.byref(desc), p, p, None, 16, None) == pg.PG_ERR_INVALID_ARG
+    assert "resp_rows" in L.pg_last_error().decode()
+    assert L.pg_unpack_rows(ctypes.byref(desc), None, p, p, 16, None) == pg.PG_ERR_INVALID_ARG
+    # 4-byte rows need only 4-byte alignment
+    no_pre, _b2 = _host_desc(((0, [3]),))
+    empty, _b3 = _host_desc(((0, [0]),))
+    assert L.pg_pack_rows(ctypes.byref(empty), None, None, None, 8, None) == pg.PG_OK
+    assert L.pg_unpack_rows(ctypes.byref(empty), None, None, None, 4, None) == pg.PG_OK
+    assert no_pre.total_prefix_rows == 0 and no_pre.total_rows == 3
+
+
 def test_python_binding_has_no_fallback():
     """The binding imports neither the oracle nor any CPU path."""
     src = open(pg.__file__).read()
