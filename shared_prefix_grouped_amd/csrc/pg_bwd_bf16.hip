@@ -150,13 +150,16 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
   wait_async_loads();
   pin(kvf);
 
-  // dV^T (role A) or dK^T (role B): register r of lane l holds
-  // d = 32 nb + mfma_row(r, hi), key = l32.
-  f32x16 acc[D / 32];
+  // dK^T and dV^T (role B): register r of lane l holds d = 32 nb +
+  // mfma_row(r, hi), key = l32.
+  f32x16 acck[D / 32], accv[D / 32];
 #pragma unroll
   for (int nb = 0; nb < D / 32; ++nb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[nb][r] = 0.f;
+    for (int r = 0; r < 16; ++r) {
+      acck[nb][r] = 0.f;
+      accv[nb][r] = 0.f;
+    }
 
   // Steps: 32-row query blocks [qa + 32 b, ...) for b = nB-1 down to 0, the
   // query heads of the kv head interleaved per block.  Walking down from
@@ -166,10 +169,18 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
   const int nB = (qb - qa + C::BM - 1) / C::BM;  // blocks per query head
   const int nS = nB * rep;
   const size_t q_row = (size_t)Hq * D;
-  auto step_of = [&](int n, int &h, int &c0) {
-    const int bi = n / rep;
-    h = hk * rep + (n - bi * rep);
-    c0 = qa + (nB - 1 - bi) * C::BM;
+  // Step n = bi * rep + j covers query head hk * rep + j and the rows
+  // [c0, c0 + 32), c0 = qa + (nB - 1 - bi) * 32; walking the steps in order
+  // is a counter and a row pointer, with no division.
+  struct Step {
+    int j, c0;
+  };
+  const Step first{0, qa + (nB - 1) * C::BM};
+  auto advance = [&](Step &st) {
+    if (++st.j == rep) {
+      st.j = 0;
+      st.c0 -= C::BM;
+    }
   };
 
   // Copies of step n into slot n % NSLOT go through registers: every thread
@@ -180,8 +191,9 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
   // of both roles for the LDS, and lose: the step would wait for them.)
   static_assert(C::BM * D / 8 == C::NT || C::BM * D / 8 == C::NT / 2,
                 "one or half a chunk of each tensor per thread and step");
+  static_assert((C::NSLOT & (C::NSLOT - 1)) == 0, "slot index by mask");
   constexpr int CPR = D / 8;                           // 16-byte chunks per row
-  const bool chunk_owner = tid < C::BM * CPR;
+  const bool chunk_owner = C::BM * CPR == C::NT || tid < C::BM * CPR;
   const int crow = tid / CPR, cch = tid % CPR;
   const int cdst = crow * D + ((cch ^ swz_chunk<D>(crow)) << 3);  // swizzled, elements
   // Buffer loads with one scalar descriptor per tensor: the row offset of
@@ -195,27 +207,31 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
   const int coff = crow * (int)(q_row * sizeof(bf16)) + cch * 16;  // thread's chunk in a step
   bf16x8 stq, sto;
   float stl = 0.f;
-  auto stage = [&](int n) {
-    int h, c0;
-    step_of(n, h, c0);
+  // The rows of the steps are staged in step order; `stg` is the next one.
+  Step stg = first;
+  auto stage = [&]() {
+    const int h = hk * rep + stg.j, c0 = stg.c0;
+    advance(stg);
     if (chunk_owner) {
       const int off = coff + c0 * (int)(q_row * sizeof(bf16));
       stq = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rQ, off, h * D * 2, 0));
       sto = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rdO, off, h * D * 2, 0));
     }
-    if (wave < 2 && lane < C::BM) {
-      // rows past the batch: an offset past the resource, read as zero
-      const int off = (c0 + lane < T) ? (h * T + c0 + lane) * 4 : 0x7fffffff;
+    if (wave < 2) {
+      // every lane loads, so no lane mask is needed: lanes past the 32 rows,
+      // and rows past the batch, use an offset past the resource (read as 0)
+      const int off = (lane < C::BM && c0 + lane < T) ? (h * T + c0 + lane) * 4 : 0x7fffffff;
       stl = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rL, off, 0, 0));
     }
   };
   auto commit = [&](int n) {
-    const int slot = n % C::NSLOT;
+    const int slot = n & (C::NSLOT - 1);
     if (chunk_owner) {
       *reinterpret_cast<bf16x8 *>(sQ + slot * C::BM * D + cdst) = stq;
       *reinterpret_cast<bf16x8 *>(sdO + slot * C::BM * D + cdst) = sto;
     }
-    if (wave < 2 && lane < C::BM) (wave == 0 ? sL : sDl)[slot * 64 + lane] = stl;
+    // lanes 32..63 land in the unused half of the 64-float slot
+    if (wave < 2) (wave == 0 ? sL : sDl)[slot * 64 + lane] = stl;
   };
   // Start of step n: every wave has finished step n-1 and slot n (written
   // in step n-2) is visible.  Then slot n+2, last read in step n-1, receives
@@ -223,10 +239,10 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
   auto open_step = [&](int n) {
     __syncthreads();
     if (n + 2 < nS) commit(n + 2);
-    if (n + 3 < nS) stage(n + 3);
+    if (n + 3 < nS) stage();
   };
-  auto slot_q = [&](int n) { return lds_bytes(sQ + (n % C::NSLOT) * C::BM * D); };
-  auto slot_do = [&](int n) { return lds_bytes(sdO + (n % C::NSLOT) * C::BM * D); };
+  auto slot_q = [&](int n) { return lds_bytes(sQ + (n & (C::NSLOT - 1)) * C::BM * D); };
+  auto slot_do = [&](int n) { return lds_bytes(sdO + (n & (C::NSLOT - 1)) * C::BM * D); };
 
   // Whether query block [c0, c0 + 32) meets the group's keys at all, and
   // whether every (query, key) pair of it is visible.
@@ -234,7 +250,7 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
   auto block_full = [&](int c0) { return (c0 >= kwl) && (c0 + 32 <= min_hi); };
 
   for (int j = 0; j < 3 && j < nS; ++j) {
-    stage(j);
+    stage();
     if (j < 2) commit(j);
   }
   // Drain the prologue's loads here: otherwise the compiler's wait analysis
@@ -245,16 +261,17 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
   pin(sto);
   pin(stl);
   if (roleA) {
-    // S -> P for step n; P (fp32) goes to LDS for wave B (which uses it in
-    // step n+1) and, packed to bf16, into dV^T += dO_n^T P_n right away.
-    // The loop runs to n = nS so that every wave meets the same barriers.
+    // S -> P for step n; P (fp32) goes to LDS for wave B, which uses it in
+    // step n+1.  The loop runs to n = nS so that every wave meets the same
+    // barriers.
+    Step cur = first;
     for (int n = 0; n <= nS; ++n) {
       open_step(n);
-      int h = 0, c0 = 0;
-      if (n < nS) step_of(n, h, c0);
+      const int c0 = cur.c0;
+      advance(cur);
       if (n < nS && block_live(c0)) {
         lds_cchar *cQ = slot_q(n);
-        const float *cL = sL + (n % C::NSLOT) * 64;
+        const float *cL = sL + (n & (C::NSLOT - 1)) * 64;
         f32x16 s;
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[r] = 0.f;
@@ -273,17 +290,10 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
               const int qr = c0 + ql + j;
               p = (key <= qr && qr < hik) ? p : 0.f;
             }
-            s[rq * 4 + j] = p;
             pq[j] = p;
           }
           sP[kg][n & 1][rq][lane] = pq;
         }
-        const bf16x8 p0 = pack8(s, 0), p1 = pack8(s, 8);
-        lds_cchar *cdO = slot_do(n);
-#pragma unroll
-        for (int nb = 0; nb < D / 32; ++nb) acc[nb] = mfma32(frag.tr(cdO, 0, nb), p0, acc[nb]);
-#pragma unroll
-        for (int nb = 0; nb < D / 32; ++nb) acc[nb] = mfma32(frag.tr(cdO, 16, nb), p1, acc[nb]);
       }
     }
   } else {
@@ -294,29 +304,46 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
     wait_async_loads();
     f32x16 dp;  // dP of the previous step
     bool live_prev = false;
+    Step cur = first;
     for (int n = 0; n <= nS; ++n) {
       open_step(n);
-      int h = 0, c0 = 0;
-      if (n < nS) step_of(n, h, c0);
+      const int c0 = cur.c0;
+      advance(cur);
       const bool live = n < nS && block_live(c0);
       if (live_prev) {
-        // dS_{n-1} = P_{n-1} * (dP_{n-1} - delta), dK^T += Q_{n-1}^T dS_{n-1}
+        // dV^T += dO_{n-1}^T P_{n-1}; dS_{n-1} = P_{n-1} * (dP_{n-1} - delta),
+        // dK^T += Q_{n-1}^T dS_{n-1}
         lds_cchar *cQ = slot_q(n - 1);
-        const float *cDl = sDl + ((n - 1) % C::NSLOT) * 64;
+        lds_cchar *cdO = slot_do(n - 1);
+        const float *cDl = sDl + ((n - 1) & (C::NSLOT - 1)) * 64;
+        f32x16 p;
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          const f32x4 pq = sP[kg][(n - 1) & 1][rq][lane];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) p[rq * 4 + j] = pq[j];
+        }
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) {
+          const bf16x8 pb = pack8(p, sub * 8);
+#pragma unroll
+          for (int nb = 0; nb < D / 32; ++nb)
+            accv[nb] = mfma32(frag.tr(cdO, sub * 16, nb), pb, accv[nb]);
+        }
 #pragma unroll
         for (int rq = 0; rq < 4; ++rq) {
           const int ql = rq * 8 + hi * 4;
           const f32x4 Dq = *reinterpret_cast<const f32x4 *>(&cDl[ql]);
-          const f32x4 pq = sP[kg][(n - 1) & 1][rq][lane];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) dp[rq * 4 + j] = pq[j] * (dp[rq * 4 + j] - Dq[j]);
+          for (int j = 0; j < 4; ++j)
+            dp[rq * 4 + j] = p[rq * 4 + j] * (dp[rq * 4 + j] - Dq[j]);
         }
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub) {
           const bf16x8 db = pack8(dp, sub * 8);
 #pragma unroll
           for (int nb = 0; nb < D / 32; ++nb)
-            acc[nb] = mfma32(frag.tr(cQ, sub * 16, nb), db, acc[nb]);
+            acck[nb] = mfma32(frag.tr(cQ, sub * 16, nb), db, acck[nb]);
         }
       }
       if (live) {
@@ -331,33 +358,38 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
     }
   }
 
-  if (!group_active || !key_ok) return;
-  const float f = roleA ? 1.f : scale;
-  if (part < 0) {
-    bf16 *dst = (roleA ? dV : dK) + ((size_t)key * Hkv + hk) * D;
+  if (roleA || !group_active || !key_ok) return;
+  // kind 0: dV, kind 1: dK (scaled)
 #pragma unroll
-    for (int nb = 0; nb < D / 32; ++nb)
+  for (int kind = 0; kind < 2; ++kind) {
+    const f32x16 *acc = kind == 0 ? accv : acck;
+    const float f = kind == 0 ? 1.f : scale;
+    if (part < 0) {
+      bf16 *dst = (kind == 0 ? dV : dK) + ((size_t)key * Hkv + hk) * D;
 #pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        const int d0 = nb * 32 + rq * 8 + hi * 4;
-        *reinterpret_cast<u32x2 *>(dst + d0) =
-            pack4_bf16(acc[nb][rq * 4 + 0] * f, acc[nb][rq * 4 + 1] * f,
-                       acc[nb][rq * 4 + 2] * f, acc[nb][rq * 4 + 3] * f);
-      }
-  } else {
-    // partial slot [part][hk][dV, dK][key - k0][d], float
-    float *dst = partial + (((size_t)part * Hkv + hk) * 2 + (roleA ? 0 : 1)) * (C::BN * D) +
-                 (size_t)(key - k0) * D;
+      for (int nb = 0; nb < D / 32; ++nb)
 #pragma unroll
-    for (int nb = 0; nb < D / 32; ++nb)
+        for (int rq = 0; rq < 4; ++rq) {
+          const int d0 = nb * 32 + rq * 8 + hi * 4;
+          *reinterpret_cast<u32x2 *>(dst + d0) =
+              pack4_bf16(acc[nb][rq * 4 + 0] * f, acc[nb][rq * 4 + 1] * f,
+                         acc[nb][rq * 4 + 2] * f, acc[nb][rq * 4 + 3] * f);
+        }
+    } else {
+      // partial slot [part][hk][dV, dK][key - k0][d], float
+      float *dst = partial + (((size_t)part * Hkv + hk) * 2 + kind) * (C::BN * D) +
+                   (size_t)(key - k0) * D;
 #pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        const int d0 = nb * 32 + rq * 8 + hi * 4;
-        f32x4 v;
+      for (int nb = 0; nb < D / 32; ++nb)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) v[j] = acc[nb][rq * 4 + j] * f;
-        *reinterpret_cast<f32x4 *>(dst + d0) = v;
-      }
+        for (int rq = 0; rq < 4; ++rq) {
+          const int d0 = nb * 32 + rq * 8 + hi * 4;
+          f32x4 v;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) v[j] = acc[nb][rq * 4 + j] * f;
+          *reinterpret_cast<f32x4 *>(dst + d0) = v;
+        }
+    }
   }
 }
 
