@@ -277,21 +277,33 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
         for (int r = 0; r < 16; ++r) s[r] = 0.f;
 #pragma unroll
         for (int st = 0; st < D / 16; ++st) s = mfma32(frag.row(cQ, 0, st), kvf[st], s);
-        const bool full = block_full(c0);
+        f32x16 p;
 #pragma unroll
         for (int rq = 0; rq < 4; ++rq) {
-          const int ql = rq * 8 + hi * 4;
-          const f32x4 Lq = *reinterpret_cast<const f32x4 *>(&cL[ql]);
+          const f32x4 Lq = *reinterpret_cast<const f32x4 *>(&cL[rq * 8 + hi * 4]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            p[rq * 4 + j] = fast_exp2(fmaf(s[rq * 4 + j], scale_log2, -Lq[j]));
+        }
+        if (!block_full(c0)) {
+          // query row c0 + 8 rq + 4 hi + j sees this key iff its distance
+          // from the key is in [0, hik - key): one unsigned compare each.
+          // (The empty asm keeps this a branch: if-converted, every block
+          // would pay for the compares.)
+          asm volatile("");
+          const int dq0 = c0 + hi * 4 - key;
+          const unsigned span = (unsigned)(hik - key);
+#pragma unroll
+          for (int rq = 0; rq < 4; ++rq)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              p[rq * 4 + j] = (unsigned)(dq0 + rq * 8 + j) < span ? p[rq * 4 + j] : 0.f;
+        }
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
           f32x4 pq;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            float p = fast_exp2(fmaf(s[rq * 4 + j], scale_log2, -Lq[j]));
-            if (!full) {
-              const int qr = c0 + ql + j;
-              p = (key <= qr && qr < hik) ? p : 0.f;
-            }
-            pq[j] = p;
-          }
+          for (int j = 0; j < 4; ++j) pq[j] = p[rq * 4 + j];
           sP[kg][n & 1][rq][lane] = pq;
         }
       }
