@@ -224,8 +224,7 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
       stl = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rL, off, 0, 0));
     }
   };
-  auto commit = [&](int n) {
-    const int slot = n & (C::NSLOT - 1);
+  auto commit = [&](int slot) {
     if (chunk_owner) {
       *reinterpret_cast<bf16x8 *>(sQ + slot * C::BM * D + cdst) = stq;
       *reinterpret_cast<bf16x8 *>(sdO + slot * C::BM * D + cdst) = sto;
@@ -233,16 +232,18 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
     // lanes 32..63 land in the unused half of the 64-float slot
     if (wave < 2) (wave == 0 ? sL : sDl)[slot * 64 + lane] = stl;
   };
-  // Start of step n: every wave has finished step n-1 and slot n (written
-  // in step n-2) is visible.  Then slot n+2, last read in step n-1, receives
-  // the rows staged in step n-1, and the rows of step n+3 are loaded.
-  auto open_step = [&](int n) {
+  // Start of step n (slot k = n mod NSLOT): every wave has finished step
+  // n-1 and slot k (written in step n-2) is visible.  Then slot k+2, last
+  // read in step n-1, receives the rows staged in step n-1, and the rows of
+  // step n+3 are loaded.  The step loops below are unrolled NSLOT times, so
+  // k, and with it every slot address, is a compile-time constant.
+  auto open_step = [&](int n, int k) {
     __syncthreads();
-    if (n + 2 < nS) commit(n + 2);
+    if (n + 2 < nS) commit((k + 2) & (C::NSLOT - 1));
     if (n + 3 < nS) stage();
   };
-  auto slot_q = [&](int n) { return lds_bytes(sQ + (n & (C::NSLOT - 1)) * C::BM * D); };
-  auto slot_do = [&](int n) { return lds_bytes(sdO + (n & (C::NSLOT - 1)) * C::BM * D); };
+  auto slot_q = [&](int k) { return lds_bytes(sQ + (k & (C::NSLOT - 1)) * C::BM * D); };
+  auto slot_do = [&](int k) { return lds_bytes(sdO + (k & (C::NSLOT - 1)) * C::BM * D); };
 
   // Whether query block [c0, c0 + 32) meets the group's keys at all, and
   // whether every (query, key) pair of it is visible.
@@ -265,13 +266,17 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
     // step n+1.  The loop runs to n = nS so that every wave meets the same
     // barriers.
     Step cur = first;
-    for (int n = 0; n <= nS; ++n) {
-      open_step(n);
+    for (int n0 = 0; n0 <= nS; n0 += C::NSLOT)
+#pragma unroll
+    for (int k = 0; k < C::NSLOT; ++k) {
+      const int n = n0 + k;
+      if (n > nS) break;
+      open_step(n, k);
       const int c0 = cur.c0;
       advance(cur);
       if (n < nS && block_live(c0)) {
-        lds_cchar *cQ = slot_q(n);
-        const float *cL = sL + (n & (C::NSLOT - 1)) * 64;
+        lds_cchar *cQ = slot_q(k);
+        const float *cL = sL + k * 64;
         f32x16 s;
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[r] = 0.f;
@@ -304,7 +309,7 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
           f32x4 pq;
 #pragma unroll
           for (int j = 0; j < 4; ++j) pq[j] = p[rq * 4 + j];
-          sP[kg][n & 1][rq][lane] = pq;
+          sP[kg][k & 1][rq][lane] = pq;
         }
       }
     }
@@ -317,21 +322,26 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
     f32x16 dp;  // dP of the previous step
     bool live_prev = false;
     Step cur = first;
-    for (int n = 0; n <= nS; ++n) {
-      open_step(n);
+    for (int n0 = 0; n0 <= nS; n0 += C::NSLOT)
+#pragma unroll
+    for (int k = 0; k < C::NSLOT; ++k) {
+      const int n = n0 + k;
+      if (n > nS) break;
+      open_step(n, k);
       const int c0 = cur.c0;
       advance(cur);
       const bool live = n < nS && block_live(c0);
+      const int kp = (k + C::NSLOT - 1) & (C::NSLOT - 1);  // slot of step n-1
       if (live_prev) {
         // dV^T += dO_{n-1}^T P_{n-1}; dS_{n-1} = P_{n-1} * (dP_{n-1} - delta),
         // dK^T += Q_{n-1}^T dS_{n-1}
-        lds_cchar *cQ = slot_q(n - 1);
-        lds_cchar *cdO = slot_do(n - 1);
-        const float *cDl = sDl + ((n - 1) & (C::NSLOT - 1)) * 64;
+        lds_cchar *cQ = slot_q(kp);
+        lds_cchar *cdO = slot_do(kp);
+        const float *cDl = sDl + kp * 64;
         f32x16 p;
 #pragma unroll
         for (int rq = 0; rq < 4; ++rq) {
-          const f32x4 pq = sP[kg][(n - 1) & 1][rq][lane];
+          const f32x4 pq = sP[kg][kp & 1][rq][lane];
 #pragma unroll
           for (int j = 0; j < 4; ++j) p[rq * 4 + j] = pq[j];
         }
@@ -360,7 +370,7 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
       }
       if (live) {
         // dP_n = dO_n V^T
-        lds_cchar *cdO = slot_do(n);
+        lds_cchar *cdO = slot_do(k);
 #pragma unroll
         for (int r = 0; r < 16; ++r) dp[r] = 0.f;
 #pragma unroll
