@@ -183,19 +183,19 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
     }
   };
 
-  // Copies of step n into slot n % NSLOT go through registers: every thread
-  // loads one 16-byte chunk of Q and of dO (and waves 0 / 1 one LSE / delta
-  // value per row) at step n-3 and stores them into LDS with ordinary LDS
-  // writes at step n-2, after the barrier that retired the slot's previous
-  // rows.  (Direct global->LDS copies would compete with the fragment reads
-  // of both roles for the LDS, and lose: the step would wait for them.)
-  static_assert(C::BM * D / 8 == C::NT || C::BM * D / 8 == C::NT / 2,
-                "one or half a chunk of each tensor per thread and step");
+  // Copies of step n into slot n % NSLOT go through registers of the role-A
+  // waves (role B carries both accumulators and has no registers to spare;
+  // it only meets the barrier): each A thread loads CPT 16-byte chunks of Q
+  // and of dO (and waves 0 / 1 one LSE / delta value per row) at step n-3
+  // and stores them into LDS with ordinary LDS writes at step n-2, after the
+  // barrier that retired the slot's previous rows.  (Direct global->LDS
+  // copies would compete with the fragment reads of both roles for the LDS,
+  // and lose: the step would wait for them.)
   static_assert((C::NSLOT & (C::NSLOT - 1)) == 0, "slot index by mask");
-  constexpr int CPR = D / 8;                           // 16-byte chunks per row
-  const bool chunk_owner = C::BM * CPR == C::NT || tid < C::BM * CPR;
-  const int crow = tid / CPR, cch = tid % CPR;
-  const int cdst = crow * D + ((cch ^ swz_chunk<D>(crow)) << 3);  // swizzled, elements
+  constexpr int CPR = D / 8;                // 16-byte chunks per row
+  constexpr int NA = C::NG * 64;            // role-A threads
+  constexpr int CPT = C::BM * CPR / NA;     // chunks per A thread and tensor
+  static_assert(CPT >= 1 && CPT * NA == C::BM * CPR, "chunks split evenly over role A");
   // Buffer loads with one scalar descriptor per tensor: the row offset of
   // the step is part of the vector offset, which the range check covers, so
   // rows past the end of the batch read as zero (the visibility mask covers
@@ -204,18 +204,25 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
   const __amdgpu_buffer_rsrc_t rQ = buffer_resource(Q, (size_t)T * q_row * sizeof(bf16));
   const __amdgpu_buffer_rsrc_t rdO = buffer_resource(dO, (size_t)T * q_row * sizeof(bf16));
   const __amdgpu_buffer_rsrc_t rL = buffer_resource(wave == 0 ? LSE2 : Delta, (size_t)Hq * T * 4);
-  const int coff = crow * (int)(q_row * sizeof(bf16)) + cch * 16;  // thread's chunk in a step
-  bf16x8 stq, sto;
+  int coff[CPT], cdst[CPT];  // chunk c of this thread: source byte offset, swizzled LDS element
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    const int i = tid + c * NA, crow = i / CPR, cch = i % CPR;
+    coff[c] = crow * (int)(q_row * sizeof(bf16)) + cch * 16;
+    cdst[c] = crow * D + ((cch ^ swz_chunk<D>(crow)) << 3);
+  }
+  bf16x8 stq[CPT], sto[CPT];
   float stl = 0.f;
   // The rows of the steps are staged in step order; `stg` is the next one.
   Step stg = first;
   auto stage = [&]() {
     const int h = hk * rep + stg.j, c0 = stg.c0;
     advance(stg);
-    if (chunk_owner) {
-      const int off = coff + c0 * (int)(q_row * sizeof(bf16));
-      stq = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rQ, off, h * D * 2, 0));
-      sto = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rdO, off, h * D * 2, 0));
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int off = coff[c] + c0 * (int)(q_row * sizeof(bf16));
+      stq[c] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rQ, off, h * D * 2, 0));
+      sto[c] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rdO, off, h * D * 2, 0));
     }
     if (wave < 2) {
       // every lane loads, so no lane mask is needed: lanes past the 32 rows,
@@ -225,18 +232,19 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
     }
   };
   auto commit = [&](int slot) {
-    if (chunk_owner) {
-      *reinterpret_cast<bf16x8 *>(sQ + slot * C::BM * D + cdst) = stq;
-      *reinterpret_cast<bf16x8 *>(sdO + slot * C::BM * D + cdst) = sto;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      *reinterpret_cast<bf16x8 *>(sQ + slot * C::BM * D + cdst[c]) = stq[c];
+      *reinterpret_cast<bf16x8 *>(sdO + slot * C::BM * D + cdst[c]) = sto[c];
     }
     // lanes 32..63 land in the unused half of the 64-float slot
     if (wave < 2) (wave == 0 ? sL : sDl)[slot * 64 + lane] = stl;
   };
   // Start of step n (slot k = n mod NSLOT): every wave has finished step
-  // n-1 and slot k (written in step n-2) is visible.  Then slot k+2, last
-  // read in step n-1, receives the rows staged in step n-1, and the rows of
-  // step n+3 are loaded.  The step loops below are unrolled NSLOT times, so
-  // k, and with it every slot address, is a compile-time constant.
+  // n-1 and slot k (written in step n-2) is visible.  Then (role A) slot k+2,
+  // last read in step n-1, receives the rows staged in step n-1, and the
+  // rows of step n+3 are loaded.  The step loops below are unrolled NSLOT
+  // times, so k, and with it every slot address, is a compile-time constant.
   auto open_step = [&](int n, int k) {
     __syncthreads();
     if (n + 2 < nS) commit((k + 2) & (C::NSLOT - 1));
@@ -250,9 +258,11 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
   auto block_live = [&](int c0) { return group_active && !(c0 + 31 < kw0 || c0 >= max_hi); };
   auto block_full = [&](int c0) { return (c0 >= kwl) && (c0 + 32 <= min_hi); };
 
-  for (int j = 0; j < 3 && j < nS; ++j) {
-    stage();
-    if (j < 2) commit(j);
+  if (roleA) {
+    for (int j = 0; j < 3 && j < nS; ++j) {
+      stage();
+      if (j < 2) commit(j);
+    }
   }
   // Drain the prologue's loads here: otherwise the compiler's wait analysis
   // carries them into the loop and waits for every step's own loads mid-step.
@@ -327,7 +337,7 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
     for (int k = 0; k < C::NSLOT; ++k) {
       const int n = n0 + k;
       if (n > nS) break;
-      open_step(n, k);
+      __syncthreads();
       const int c0 = cur.c0;
       advance(cur);
       const bool live = n < nS && block_live(c0);
