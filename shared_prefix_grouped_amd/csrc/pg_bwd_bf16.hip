@@ -585,15 +585,24 @@ __global__ __launch_bounds__(256, 2) void dq_bf16_kernel(
       }
       // register r holds key c0 + b*32 + mfma_row(r, hi); the lane's column is its query
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float p = fast_exp2(fmaf(s[r], scale_log2, negL));
-        if (!full) {
-          const int kr = c0 + b * 32 + mfma_row(r, hi);
-          const bool ok = kr < cend && kr <= qrow && (kr < pe || kr >= lo);
-          p = ok ? p : 0.f;
+      for (int r = 0; r < 16; ++r) s[r] = fast_exp2(fmaf(s[r], scale_log2, negL));
+      if (!full) {
+        // key kr is visible iff kr <= kmax (its chunk end and the query) and
+        // it is not in [pe, lo), the responses before the query's own.  (The
+        // empty asm keeps this a branch, taken by partial chunks only.)
+        asm volatile("");
+        const int kb = c0 + b * 32 + 4 * hi;
+        const int kmax = min(cend - 1, qrow) - kb;
+        const unsigned gap = (unsigned)max(lo - pe, 0);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kr = mfma_row(r, 0);  // key - kb
+          const bool ok = kr <= kmax && (unsigned)(kr + kb - pe) >= gap;
+          s[r] = ok ? s[r] : 0.f;
         }
-        s[r] = p * (dp[r] - Dq);
       }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = s[r] * (dp[r] - Dq);
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub) {
         const bf16x8 db = pack8(s, sub * 8);

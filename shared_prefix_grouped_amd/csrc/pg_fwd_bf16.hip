@@ -126,7 +126,12 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   float m = kMasked, l = 0.f;
 
   if (nC > 0) issue(0);
-  for (int ci = 0; ci < nC; ++ci) {
+  // unrolled over the two buffers, so buffer addresses are immediates
+  for (int ci0 = 0; ci0 < nC; ci0 += 2)
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int ci = ci0 + u;
+    if (ci >= nC) break;
     int c0, cend;
     chunk_range(ci, c0, cend);
     // chunk ci has landed for every wave, and every wave is done reading the
@@ -134,8 +139,8 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
     wait_async_loads();
     __syncthreads();
     if (ci + 1 < nC) issue(ci + 1);
-    lds_cchar *cK = lds_bytes(sK + (ci & 1) * C::BN * D);
-    lds_cchar *cV = lds_bytes(sV + (ci & 1) * C::BN * D);
+    lds_cchar *cK = lds_bytes(sK + u * C::BN * D);
+    lds_cchar *cV = lds_bytes(sV + u * C::BN * D);
     if (!wave_active) continue;
     const int clast = min(c0 + C::BN, cend) - 1;
     if (c0 > qwl) continue;                       // every key follows every row
