@@ -151,14 +151,14 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
     // S^T = K Q^T for two 32-key blocks
     f32x16 s[2];
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
+    for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[b][r] = 0.f;
+    // both key blocks per k-step: consecutive MFMAs are independent
 #pragma unroll
-      for (int st = 0; st < D / 16; ++st) {
-        s[b] = mfma32(frag.row(cK, b * 32, st), qf[st], s[b]);
-      }
-    }
+    for (int st = 0; st < D / 16; ++st)
+#pragma unroll
+      for (int b = 0; b < 2; ++b) s[b] = mfma32(frag.row(cK, b * 32, st), qf[st], s[b]);
     if (!full) {
 #pragma unroll
       for (int b = 0; b < 2; ++b)
