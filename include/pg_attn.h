@@ -220,8 +220,8 @@ size_t pg_attn_bwd_workspace_size(const pg_desc *d, pg_dtype t);
  * given to pg_attn_fwd; outputs dq [T,Hq,d], dk, dv [T,Hkv,d] are fully
  * overwritten.  `workspace` is device scratch of at least
  * pg_attn_bwd_workspace_size bytes (contents need not be initialised).
- * PG_BF16 needs (T + 32) * Hq * d * 2 < 2^31 (q and dout under 2 GiB each:
- * the dK/dV kernel addresses them with 32-bit signed buffer offsets), else
+ * PG_BF16 needs (T + 32) * Hq * d * 2 < 2^32 (q and dout under 4 GiB each:
+ * the dK/dV kernel addresses them with 32-bit unsigned buffer offsets), else
  * PG_ERR_UNSUPPORTED. */
 pg_status pg_attn_bwd(const pg_desc *d, pg_dtype t, float softmax_scale, const void *q,
                       const void *k, const void *v, const void *o, const float *lse,

@@ -601,9 +601,9 @@ pg_status pg_attn_bwd(const pg_desc *d, pg_dtype t, float softmax_scale, const v
                         {dq, "dq"}, {dk, "dk"}, {dv, "dv"}, {workspace, "workspace"}})) != PG_OK)
     return st;
   if (t == PG_BF16 && (size_t(d->total_rows) + 32) * size_t(d->num_q_heads) *
-                             size_t(d->head_dim) * 2 > size_t(INT32_MAX))
+                             size_t(d->head_dim) * 2 > size_t(UINT32_MAX))
     return fail(PG_ERR_UNSUPPORTED,
-                "bf16 backward: q and dout must each be under 2 GiB (32-bit buffer offsets)");
+                "bf16 backward: q and dout must each be under 4 GiB (32-bit buffer offsets)");
   const size_t need = pg_attn_bwd_workspace_size(d, t);
   if (ws_bytes < need)
     return fail(PG_ERR_WORKSPACE, "workspace too small: need " + std::to_string(need) +

@@ -220,7 +220,8 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
     advance(stg);
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
-      const int off = coff[c] + c0 * (int)(q_row * sizeof(bf16));
+      // unsigned: the offset is a 32-bit unsigned byte count (tensors up to 4 GiB)
+      const int off = (int)((uint32_t)coff[c] + (uint32_t)c0 * (uint32_t)(q_row * sizeof(bf16)));
       stq[c] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rQ, off, h * D * 2, 0));
       sto[c] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rdO, off, h * D * 2, 0));
     }

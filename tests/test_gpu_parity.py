@@ -281,3 +281,43 @@ def test_empty_batch():
     dq, dk, dv = pg.pg_attn_bwd(batch, q, q.clone(), q.clone(), o, lse, q.clone())
     torch.cuda.synchronize()
     assert o.shape == (0, 2, 64) and dq.shape == (0, 2, 64)
+
+
+def test_bf16_tensors_over_2gib():
+    """Q and dO of 2.3 GB each (17 copies of a 16384-row prefix + 256-row
+    response, GQA 32/8): the dK/dV kernel's 32-bit buffer offsets pass 2^31.
+    The last group, whose rows all lie past 2 GiB, is checked against the
+    oracle on sampled query rows and on key rows near the prefix end and in
+    the response (each seen by at most 257 query rows)."""
+    import shared_prefix_grouped_amd as pg
+    P, R, G, hq, hkv, d = 16384, 256, 17, 32, 8, 128
+    groups = [(P, [R])] * G
+    T = G * (P + R)
+    assert (T - (P + R)) * hq * d * 2 > 2 ** 31  # the last group starts past 2 GiB
+    _say(f"[parity] over-2GiB: T={T}, q bytes {T * hq * d * 2 / 2**30:.2f} GiB")
+    gen = torch.Generator(device="cuda").manual_seed(21)
+    q, k, v, do = (torch.randn((T, h, d), generator=gen, device="cuda").to(torch.bfloat16)
+                   for h in (hq, hkv, hkv, hq))
+    batch = pg.pg_pack(groups, hq, hkv, d)
+    o, lse = pg.pg_attn_fwd(batch, q, k, v)
+    dq, dk, dv = pg.pg_attn_bwd(batch, q, k, v, o, lse, do)
+    torch.cuda.synchronize()
+    g0 = T - (P + R)
+    sub = {n: x[g0:].float().cpu().numpy() for n, x in (("q", q), ("k", k), ("v", v), ("do", do))}
+    one = [(P, [R])]
+    rows = [0, 1, P - 1, P, P + 1, P + R - 1, 5000, 12345]
+    heads = [0, 31]
+    ref = repeated_prefix_rows(one, sub["q"], sub["k"], sub["v"], sub["do"], rows, heads)
+    gr = [g0 + r for r in rows]
+    e_o = float(np.max(np.abs(to_np(o[gr][:, heads]) - ref["o"])))
+    e_l = float(np.max(np.abs(to_np(lse[heads][:, gr]) - ref["lse"])))
+    e_q = rel_fro(to_np(dq[gr][:, heads]), ref["dq"])
+    _say(f"[parity] over-2GiB: o {e_o:.3e}, lse {e_l:.3e}, dq rel-fro {e_q:.3e}")
+    assert e_o <= 2e-2 and e_l <= 1e-3 and e_q <= 1e-2
+    krows = [P - 2, P - 1, P, P + 100, P + R - 1]
+    kref = repeated_prefix_key_rows(one, sub["q"], sub["k"], sub["v"], sub["do"], krows, [0, 7])
+    gk = [g0 + r for r in krows]
+    e_k = rel_fro(to_np(dk[gk][:, [0, 7]]), kref["dk"])
+    e_v = rel_fro(to_np(dv[gk][:, [0, 7]]), kref["dv"])
+    _say(f"[parity] over-2GiB: dk rel-fro {e_k:.3e}, dv rel-fro {e_v:.3e}")
+    assert e_k <= 1e-2 and e_v <= 1e-2
