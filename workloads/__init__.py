@@ -29,9 +29,9 @@ from typing import Dict, List, Optional, Sequence, Tuple
 import numpy as np
 
 __all__ = [
-    "Group", "AttnWorkload", "DecoderWorkload", "attention_workloads",
-    "decoder_workload", "round_to_bf16", "bf16_bits", "draw_attention_inputs",
-    "draw_decoder_inputs", "scaled_down",
+    "Group", "AttnWorkload", "DecoderWorkload", "HeadWorkload", "attention_workloads",
+    "decoder_workload", "head_workloads", "round_to_bf16", "bf16_bits", "draw_attention_inputs",
+    "draw_decoder_inputs", "draw_head_inputs", "scaled_down",
 ]
 
 
@@ -86,6 +86,24 @@ class DecoderWorkload:
         return sum(g.rows for g in self.groups)
 
 
+@dataclass(frozen=True)
+class HeadWorkload:
+    """The response log-probability head of a GRPO step: packed hidden states
+    [T, d_model] of the last layer, an LM head [vocab, d_model], token ids and
+    one reward per response."""
+    name: str
+    groups: Tuple[Group, ...]
+    d_model: int
+    vocab: int
+    seed: int
+    weight_std: float = 0.02
+    description: str = ""
+
+    @property
+    def total_rows(self) -> int:
+        return sum(g.rows for g in self.groups)
+
+
 def _ragged(rng: np.random.Generator, lo: int, hi: int, n: int) -> Tuple[int, ...]:
     return tuple(int(x) for x in rng.integers(lo, hi + 1, size=n))
 
@@ -126,6 +144,36 @@ def decoder_workload() -> DecoderWorkload:
     return DecoderWorkload("decoder_4l_g16_p2048", (Group(2048, (128,) * 16),),
                            num_layers=4, d_model=2048, num_heads=16, head_dim=128,
                            ffn_dim=5632, seed=5)
+
+
+def head_workloads() -> Dict[str, HeadWorkload]:
+    """Log-probability head workloads.  The full one reuses the layout of the
+    GQA attention workload (P = 8192, 16 responses drawn from seed 3) with a
+    2048-wide model and a 32000-token vocabulary (the pages name neither; a
+    common 7B-class head size)."""
+    rng = np.random.default_rng(3)
+    layout = (Group(8192, _ragged(rng, 64, 1024, 16)),)
+    return {
+        "grpo_head_g16_p8192": HeadWorkload(
+            "grpo_head_g16_p8192", layout, 2048, 32000, seed=7,
+            description="GRPO log-prob head: bf16, 1 group, G=16, P=8192, responses in [64,1024], "
+                        "d_model=2048, vocab=32000"),
+    }
+
+
+def draw_head_inputs(w: HeadWorkload) -> Dict[str, np.ndarray]:
+    """Hidden states [T, d_model] ~ N(0,1), LM head [vocab, d_model] ~
+    N(0, std^2) (both bf16-rounded), token ids [T] uniform in [0, vocab), one
+    reward ~ N(0,1) per response (float32), in that order."""
+    rng = np.random.default_rng(w.seed)
+    T = w.total_rows
+    hidden = round_to_bf16(rng.standard_normal((T, w.d_model), dtype=np.float32))
+    weight = round_to_bf16(rng.standard_normal((w.vocab, w.d_model), dtype=np.float32)
+                           * np.float32(w.weight_std))
+    tokens = rng.integers(0, w.vocab, size=T).astype(np.int32)
+    n_resp = sum(len(g.resp_lens) for g in w.groups)
+    rewards = rng.standard_normal(n_resp, dtype=np.float32)
+    return {"hidden": hidden, "weight": weight, "tokens": tokens, "rewards": rewards}
 
 
 def round_to_bf16(x: np.ndarray) -> np.ndarray:
