@@ -129,6 +129,17 @@ typedef struct {
  *   prefix_before [num_groups + 1]: prefix rows of the groups before g
  *                (prefix_before[num_groups] = total_prefix_rows), the
  *                offsets of pg_pack_rows' prefix buffer.
+ *   scored_row, scored_pred, scored_resp [num_scored]: the response rows
+ *                whose token the log-probability head scores, in packed
+ *                order; the row whose logits score it (the previous position
+ *                of its baseline sequence [P; R_i]: the previous response row,
+ *                or for a response's first token the group's last prefix row,
+ *                shared by all G responses); and its response index.  The
+ *                first token of a response of an empty-prefix group has no
+ *                predicting position and is not scored.
+ *   pred_start [T + 1], pred_list [num_scored]: for packed row t, the
+ *                scored entries it predicts are pred_list[pred_start[t] ..
+ *                pred_start[t + 1]), in increasing order.
  *   pairs           unmasked (query, key) pairs per query head;
  *   baseline_pairs  the same count for the repeated-prefix layout (each
  *                   [P; R_i] on its own). */
@@ -138,6 +149,7 @@ typedef struct {
   int32_t num_q_tiles, num_kv_tiles;
   int32_t num_kv_items, num_kv_sums, num_kv_parts;
   int32_t total_prefix_rows;
+  int32_t num_scored;
   int64_t pairs, baseline_pairs;
   const int32_t *row_lo;
   const int32_t *row_hi;
@@ -151,6 +163,11 @@ typedef struct {
   const int32_t *resp_start;
   const int32_t *resp_len;
   const int32_t *resp_group;
+  const int32_t *scored_row;
+  const int32_t *scored_pred;
+  const int32_t *scored_resp;
+  const int32_t *pred_start;
+  const int32_t *pred_list;
   size_t buf_bytes; /* bytes of the buffer actually used */
 } pg_desc;
 
@@ -238,6 +255,49 @@ pg_status pg_attn_bwd(const pg_desc *d, pg_dtype t, float softmax_scale, const v
 pg_status pg_rope(const pg_desc *d, pg_dtype t, void *x, int32_t num_heads, int32_t head_dim,
                   const int32_t *pos_ids, float theta, int32_t inverse, void *stream);
 
+/* ---- Response log-probability head of the GRPO step (skillsmp.com
+ * "prefix-grouper-grpo", "Step 4: Training Integration with GRPO"): the
+ * log-softmax of the logits over the vocabulary, gathered at each response
+ * token, summed per response, and the policy loss -mean_i(A_i * sum_i).
+ * Only scored rows are computed (pg_desc's scored_row / scored_pred: the
+ * logits of the row before each response token in its baseline sequence
+ * [P; R_i]; a response's first token is scored by the group's last prefix
+ * row).  Logits are hidden @ weight^T (LM head without bias), bf16 operands,
+ * fp32 accumulation; the products run as rocBLAS GEMMs, the rest in this
+ * library's kernels.  hidden: bf16 [T, d_model] in packed order; weight:
+ * bf16 [vocab, d_model]; tokens: int32 [T] token id of every packed row
+ * (read only at scored rows; an id outside [0, vocab) gives logp = NaN).
+ * d_model a multiple of 8.  Device buffers, 16-byte aligned, caller-owned. */
+
+/* Bytes of scratch pg_logprob_fwd / pg_logprob_bwd need: the logits of the
+ * scored rows (fp32 [num_scored, vocab]), their gradient (bf16, same shape),
+ * the gathered predicting rows (bf16) and their gradient (fp32
+ * [num_scored, d_model]), 256-byte aligned.  0 if the arguments are invalid. */
+size_t pg_logprob_workspace_size(const pg_desc *d, int32_t vocab, int32_t d_model);
+
+/* logp [num_scored]: log-probability of each scored token; lse
+ * [num_scored]: logsumexp of its logits (kept for the backward). */
+pg_status pg_logprob_fwd(const pg_desc *d, const void *hidden, const void *weight, int32_t vocab,
+                         int32_t d_model, const int32_t *tokens, float *logp, float *lse,
+                         void *workspace, size_t ws_bytes, void *stream);
+
+/* Policy loss from the log-probabilities and one advantage per response
+ * (float [num_resp], treated as a constant): loss[0] = -mean_i(A_i * S_i)
+ * with S_i the sum of response i's logp, and dlogp [num_scored] =
+ * d loss / d logp = -A_i / num_resp.  One workgroup, fixed order. */
+pg_status pg_grpo_loss(const pg_desc *d, const float *logp, const float *advantages, float *loss,
+                       float *dlogp, void *stream);
+
+/* Backward of sum_k dlogp[k] * logp[k]: dhidden fp32 [T, d_model] (every row
+ * written: zero for rows that score nothing; a group's last prefix row sums
+ * the first tokens of its G responses, in response order) and dweight fp32
+ * [vocab, d_model].  Recomputes the logits (same workspace size as the
+ * forward; contents need not be kept between the calls). */
+pg_status pg_logprob_bwd(const pg_desc *d, const void *hidden, const void *weight, int32_t vocab,
+                         int32_t d_model, const int32_t *tokens, const float *lse,
+                         const float *dlogp, float *dhidden, float *dweight, void *workspace,
+                         size_t ws_bytes, void *stream);
+
 /* Kernel timing for benchmarks.  While enabled, every kernel the library
  * launches is bracketed by two HIP events recorded on the stream it is
  * launched on.  pg_kernel_timing(1) clears the counters and enables,
@@ -252,7 +312,10 @@ pg_status pg_rope(const pg_desc *d, pg_dtype t, void *x, int32_t num_heads, int3
 #define PG_KERNEL_BWD_DQ 3
 #define PG_KERNEL_ROPE 4
 #define PG_KERNEL_ROWS 5
-#define PG_KERNEL_COUNT 6
+#define PG_KERNEL_HEAD_FWD 6
+#define PG_KERNEL_HEAD_BWD 7
+#define PG_KERNEL_LOSS 8
+#define PG_KERNEL_COUNT 9
 pg_status pg_kernel_timing(int32_t enable);
 pg_status pg_kernel_times(int32_t kernel_id, int64_t *launches, double *total_ms);
 const char *pg_kernel_name(int32_t kernel_id);

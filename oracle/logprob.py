@@ -148,3 +148,40 @@ def baseline_logprob_grads(groups, hidden, W, tokens, dlogp: np.ndarray) -> Dict
         dh[rows] += dz @ Wd
         dW += dz.T @ X
     return {"dhidden": dh, "dW": dW}
+
+
+def sampled_head(groups, hidden, W, tokens, dlogp, k_sample, hid_sample, vocab_sample,
+                 row_block: int = 256) -> Dict[str, np.ndarray]:
+    """The same quantities at sampled indices, for sizes where the full
+    per-member computation is too slow: logp and lse at scored entries
+    k_sample (order of scored_rows), the hidden-state gradient at packed rows
+    hid_sample, and the LM-head gradient at vocabulary rows vocab_sample.
+    Each scored token only depends on its predicting row (the next-token
+    reading above), so this computes, in fp64, the logits of predicting rows
+    in blocks (keeping only their logsumexp) and then the sampled sums of the
+    chain rule of baseline_logprob_grads."""
+    tgt, pred = scored_rows(groups)
+    Wd = np.asarray(W, dtype=np.float64)
+    H = np.asarray(hidden, dtype=np.float64)
+    n = tgt.size
+    lse = np.empty(n)
+    for b0 in range(0, n, row_block):
+        z = H[pred[b0:b0 + row_block]] @ Wd.T
+        m = z.max(axis=1, keepdims=True)
+        lse[b0:b0 + row_block] = (m + np.log(np.exp(z - m).sum(axis=1, keepdims=True)))[:, 0]
+    ks = np.asarray(k_sample, dtype=np.int64)
+    zt = np.einsum("kd,kd->k", H[pred[ks]], Wd[np.asarray(tokens)[tgt[ks]]])
+    out = {"logp": zt - lse[ks], "lse": lse[ks]}
+    # dhidden[t] = sum over entries k predicted by t of dlogp_k (W[tok_k] - softmax_k W)
+    dh = np.zeros((len(hid_sample), Wd.shape[1]))
+    for i, t in enumerate(hid_sample):
+        for k in np.nonzero(pred == int(t))[0]:
+            p = np.exp(H[t] @ Wd.T - lse[k])
+            dh[i] += dlogp[k] * (Wd[int(tokens[tgt[k]])] - p @ Wd)
+    out["dhidden"] = dh
+    # dW[v] = sum_k dlogp_k ([v == tok_k] - p_kv) h_pred_k
+    vs = np.asarray(vocab_sample, dtype=np.int64)
+    pv = np.exp(H[pred] @ Wd[vs].T - lse[:, None])            # [n, len(vs)]
+    onehot = (np.asarray(tokens)[tgt][:, None] == vs[None, :]).astype(np.float64)
+    out["dW"] = ((onehot - pv) * np.asarray(dlogp)[:, None]).T @ H[pred]
+    return out

@@ -36,9 +36,11 @@ PG_TILE_KV = 128
 
 EXPORTED = ("pg_pack_buffer_size", "pg_pack", "pg_pack_host", "pg_attn_fwd",
             "pg_attn_bwd_workspace_size", "pg_attn_bwd", "pg_rope", "pg_pack_rows",
-            "pg_unpack_rows", "pg_kernel_timing",
+            "pg_unpack_rows", "pg_logprob_workspace_size", "pg_logprob_fwd", "pg_grpo_loss",
+            "pg_logprob_bwd", "pg_kernel_timing",
             "pg_kernel_times", "pg_kernel_name", "pg_last_error", "pg_version")
-KERNELS = ("fwd", "bwd_pre", "bwd_dkdv", "bwd_dq", "rope", "rows")
+KERNELS = ("fwd", "bwd_pre", "bwd_dkdv", "bwd_dq", "rope", "rows", "head_fwd", "head_bwd",
+           "grpo_loss")
 
 
 class LibraryNotBuilt(RuntimeError):
@@ -67,12 +69,15 @@ class PgDesc(ctypes.Structure):
                 ("num_q_tiles", ctypes.c_int32), ("num_kv_tiles", ctypes.c_int32),
                 ("num_kv_items", ctypes.c_int32), ("num_kv_sums", ctypes.c_int32),
                 ("num_kv_parts", ctypes.c_int32), ("total_prefix_rows", ctypes.c_int32),
+                ("num_scored", ctypes.c_int32),
                 ("pairs", ctypes.c_int64), ("baseline_pairs", ctypes.c_int64),
                 ("row_lo", _i32p), ("row_hi", _i32p), ("q_tiles", _i32p), ("kv_tiles", _i32p),
                 ("kv_items", _i32p), ("kv_sums", _i32p),
                 ("group_start", _i32p), ("prefix_end", _i32p), ("prefix_before", _i32p),
                 ("resp_start", _i32p),
-                ("resp_len", _i32p), ("resp_group", _i32p), ("buf_bytes", ctypes.c_size_t)]
+                ("resp_len", _i32p), ("resp_group", _i32p), ("scored_row", _i32p),
+                ("scored_pred", _i32p), ("scored_resp", _i32p), ("pred_start", _i32p),
+                ("pred_list", _i32p), ("buf_bytes", ctypes.c_size_t)]
 
 
 _lib = None
@@ -107,6 +112,14 @@ def lib() -> ctypes.CDLL:
     L.pg_pack_rows.restype = ctypes.c_int
     L.pg_unpack_rows.argtypes = [Dp, vp, vp, vp, sz, vp]
     L.pg_unpack_rows.restype = ctypes.c_int
+    L.pg_logprob_workspace_size.argtypes = [Dp, i32, i32]
+    L.pg_logprob_workspace_size.restype = sz
+    L.pg_logprob_fwd.argtypes = [Dp, vp, vp, i32, i32, vp, vp, vp, vp, sz, vp]
+    L.pg_logprob_fwd.restype = ctypes.c_int
+    L.pg_grpo_loss.argtypes = [Dp, vp, vp, vp, vp, vp]
+    L.pg_grpo_loss.restype = ctypes.c_int
+    L.pg_logprob_bwd.argtypes = [Dp, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.pg_logprob_bwd.restype = ctypes.c_int
     L.pg_kernel_timing.argtypes = [i32]
     L.pg_kernel_timing.restype = ctypes.c_int
     L.pg_kernel_times.argtypes = [i32, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_double)]
@@ -216,6 +229,9 @@ def pg_pack_host(groups: Sequence, num_q_heads: int, num_kv_heads: int, head_dim
         "q_tiles": arr(d.q_tiles, d.num_q_tiles, 4), "kv_tiles": arr(d.kv_tiles, d.num_kv_tiles, 4),
         "kv_items": arr(d.kv_items, d.num_kv_items, 8), "kv_sums": arr(d.kv_sums, d.num_kv_sums, 4),
         "num_kv_parts": d.num_kv_parts,
+        "scored_row": arr(d.scored_row, d.num_scored), "scored_pred": arr(d.scored_pred, d.num_scored),
+        "scored_resp": arr(d.scored_resp, d.num_scored), "pred_start": arr(d.pred_start, T + 1),
+        "pred_list": arr(d.pred_list, d.num_scored),
         "group_start": arr(d.group_start, d.num_groups + 1), "prefix_end": arr(d.prefix_end, d.num_groups),
         "prefix_before": arr(d.prefix_before, d.num_groups + 1), "total_prefix_rows": d.total_prefix_rows,
         "resp_start": arr(d.resp_start, d.num_resp), "resp_len": arr(d.resp_len, d.num_resp),
@@ -343,6 +359,69 @@ def pg_unpack_rows(batch: PackedBatch, packed_rows):
     _check(lib().pg_unpack_rows(ctypes.byref(d), _vp(packed_rows), _vp(pre), _vp(resp), row_bytes,
                                 _stream_ptr(packed_rows.device)))
     return pre, resp
+
+
+def _head_args(batch, hidden, weight, tokens):
+    torch = _torch()
+    d = batch.desc
+    if hidden.dtype != torch.bfloat16 or weight.dtype != torch.bfloat16:
+        raise PgError(PG_ERR_INVALID_ARG, "hidden and weight must be bfloat16")
+    if hidden.dim() != 2 or hidden.shape[0] != d.total_rows or not hidden.is_contiguous():
+        raise PgError(PG_ERR_INVALID_ARG, "hidden must be contiguous [T, d_model]")
+    if weight.dim() != 2 or weight.shape[1] != hidden.shape[1] or not weight.is_contiguous():
+        raise PgError(PG_ERR_INVALID_ARG, "weight must be contiguous [vocab, d_model]")
+    if tokens.dtype != torch.int32 or tokens.shape != (d.total_rows,) or not tokens.is_contiguous():
+        raise PgError(PG_ERR_INVALID_ARG, "tokens must be contiguous int32 [T]")
+    return d, int(weight.shape[0]), int(hidden.shape[1])
+
+
+def _head_workspace(d, vocab, d_model, device, workspace):
+    torch = _torch()
+    need = lib().pg_logprob_workspace_size(ctypes.byref(d), vocab, d_model)
+    if need == 0:
+        raise PgError(PG_ERR_INVALID_ARG, lib().pg_last_error().decode())
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    return workspace, need
+
+
+def pg_logprob_fwd(batch: PackedBatch, hidden, weight, tokens, workspace=None):
+    """(logp, lse), float [num_scored] each: log-probability of every scored
+    response token and the logsumexp of the logits that score it."""
+    torch = _torch()
+    d, vocab, d_model = _head_args(batch, hidden, weight, tokens)
+    n = d.num_scored
+    logp = torch.empty(max(n, 1), dtype=torch.float32, device=hidden.device)
+    lse = torch.empty(max(n, 1), dtype=torch.float32, device=hidden.device)
+    ws, need = _head_workspace(d, vocab, d_model, hidden.device, workspace)
+    _check(lib().pg_logprob_fwd(ctypes.byref(d), _vp(hidden), _vp(weight), vocab, d_model,
+                                _vp(tokens), _vp(logp), _vp(lse), _vp(ws), need,
+                                _stream_ptr(hidden.device)))
+    return logp[:n], lse[:n]
+
+
+def pg_grpo_loss(batch: PackedBatch, logp, advantages):
+    """(loss [1], dlogp [num_scored]) of -mean_i(A_i * sum of response i's logp)."""
+    torch = _torch()
+    d = batch.desc
+    loss = torch.empty(1, dtype=torch.float32, device=advantages.device)
+    dlogp = torch.empty(max(d.num_scored, 1), dtype=torch.float32, device=advantages.device)
+    _check(lib().pg_grpo_loss(ctypes.byref(d), _vp(logp), _vp(advantages), _vp(loss), _vp(dlogp),
+                              _stream_ptr(advantages.device)))
+    return loss, dlogp[:d.num_scored]
+
+
+def pg_logprob_bwd(batch: PackedBatch, hidden, weight, tokens, lse, dlogp, workspace=None):
+    """(dhidden fp32 [T, d_model], dweight fp32 [vocab, d_model])."""
+    torch = _torch()
+    d, vocab, d_model = _head_args(batch, hidden, weight, tokens)
+    dh = torch.empty((max(d.total_rows, 1), d_model), dtype=torch.float32, device=hidden.device)
+    dw = torch.empty((vocab, d_model), dtype=torch.float32, device=hidden.device)
+    ws, need = _head_workspace(d, vocab, d_model, hidden.device, workspace)
+    _check(lib().pg_logprob_bwd(ctypes.byref(d), _vp(hidden), _vp(weight), vocab, d_model,
+                                _vp(tokens), _vp(lse), _vp(dlogp), _vp(dh), _vp(dw), _vp(ws), need,
+                                _stream_ptr(hidden.device)))
+    return dh[:d.total_rows], dw
 
 
 def pg_kernel_timing(enable: bool) -> None:

@@ -25,7 +25,8 @@ ARCH = "gfx950"
 
 EXTRA: list = []  # e.g. ["-Rpass-analysis=kernel-resource-usage"] to print register use
 
-SOURCES = ["pg_api.cpp", "pg_fwd_bf16.hip", "pg_bwd_bf16.hip", "pg_f32.hip", "pg_rows.hip"]
+SOURCES = ["pg_api.cpp", "pg_fwd_bf16.hip", "pg_bwd_bf16.hip", "pg_f32.hip", "pg_rows.hip",
+           "pg_head.hip"]
 
 # Packed-fp32 VALU instructions are switched off for all device code: the
 # compiler otherwise forms v_pk_{add,mul,fma}_f32 from plain float code.
@@ -61,7 +62,8 @@ def build(jobs: int = 4, verbose: bool = False) -> str:
     with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
+    # rocBLAS: the plain GEMMs of the log-probability head
+    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs + ["-lrocblas"]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -9,9 +9,11 @@
 // token sees the whole prefix and its own response up to itself).
 
 #include <hip/hip_runtime.h>
+#include <rocblas/rocblas.h>
 
 #include <algorithm>
 #include <cmath>
+#include <map>
 #include <mutex>
 #include <cstdio>
 #include <cstring>
@@ -37,11 +39,12 @@ size_t align16(size_t x) { return (x + 15) & ~size_t(15); }
 // Byte offsets of each array inside the descriptor buffer.
 struct Layout {
   size_t row_lo, row_hi, q_tiles, kv_tiles, kv_items, kv_sums, group_start, prefix_end,
-      prefix_before, resp_start, resp_len, resp_group, total;
+      prefix_before, resp_start, resp_len, resp_group, scored_row, scored_pred, scored_resp,
+      pred_start, pred_list, total;
 };
 
 Layout make_layout(int64_t T, int64_t n_groups, int64_t n_resp, int64_t n_qt, int64_t n_kvt,
-                   int64_t n_items, int64_t n_sums) {
+                   int64_t n_items, int64_t n_sums, int64_t n_scored) {
   Layout L{};
   size_t off = 0;
   auto take = [&](size_t &field, int64_t n_int32) {
@@ -60,6 +63,11 @@ Layout make_layout(int64_t T, int64_t n_groups, int64_t n_resp, int64_t n_qt, in
   take(L.resp_start, n_resp);
   take(L.resp_len, n_resp);
   take(L.resp_group, n_resp);
+  take(L.scored_row, n_scored);
+  take(L.scored_pred, n_scored);
+  take(L.scored_resp, n_scored);
+  take(L.pred_start, T + 1);
+  take(L.pred_list, n_scored);
   L.total = std::max<size_t>(off, 16);
   return L;
 }
@@ -132,6 +140,9 @@ struct HostPlan {
   int64_t T = 0, n_resp = 0, pairs = 0, base_pairs = 0;
   int32_t n_parts = 0;
   std::vector<int32_t> row_lo, row_hi, pos, gstart, pend, pbefore, rstart, rlen, rgroup;
+  // scored response rows (log-probability head): target row, predicting row,
+  // response index; and per packed row the scored entries it predicts (CSR)
+  std::vector<int32_t> sc_row, sc_pred, sc_resp, pred_start, pred_list;
   std::vector<Tile> qt, kvt;
   std::vector<KvItem> items;
   std::vector<int32_t> sums;  // 4 per split tile
@@ -178,6 +189,13 @@ pg_status plan_batch(const pg_groups *g, HostPlan &hp) {
         row_lo[x] = s;
         row_hi[x] = s + R;
         hp.pos[x] = P + (x - s);
+        // the token at baseline position P + j is scored by position P + j - 1:
+        // the previous response row, or for j = 0 the group's last prefix row
+        if (x > s || P > 0) {
+          hp.sc_row.push_back(x);
+          hp.sc_pred.push_back(x > s ? x - 1 : pe - 1);
+          hp.sc_resp.push_back(ri);
+        }
       }
       hp.pairs += int64_t(R) * P + int64_t(R) * (R + 1) / 2;
       const int64_t Lb = int64_t(P) + R;
@@ -206,6 +224,15 @@ pg_status plan_batch(const pg_groups *g, HostPlan &hp) {
     t = gend;
   }
   hp.gstart[g->num_groups] = t;
+  // predicting row -> scored entries, in entry order
+  hp.pred_start.assign(T + 1, 0);
+  for (int32_t p : hp.sc_pred) ++hp.pred_start[p + 1];
+  for (int64_t x = 0; x < T; ++x) hp.pred_start[x + 1] += hp.pred_start[x];
+  hp.pred_list.assign(hp.sc_pred.size(), 0);
+  {
+    std::vector<int32_t> fill(hp.pred_start.begin(), hp.pred_start.end() - (T > 0 ? 1 : 0));
+    for (size_t k = 0; k < hp.sc_pred.size(); ++k) hp.pred_list[fill[hp.sc_pred[k]]++] = int32_t(k);
+  }
 
   // dK/dV work items (packed order), cutting the tiles whose walk is too long
   int64_t total = 0;
@@ -246,7 +273,8 @@ pg_status plan_batch(const pg_groups *g, HostPlan &hp) {
 
 Layout layout_of(const pg_groups *g, const HostPlan &hp) {
   return make_layout(hp.T, g->num_groups, hp.n_resp, int64_t(hp.qt.size()), int64_t(hp.kvt.size()),
-                     int64_t(hp.items.size()), int64_t(hp.sums.size() / 4));
+                     int64_t(hp.items.size()), int64_t(hp.sums.size() / 4),
+                     int64_t(hp.sc_row.size()));
 }
 
 // Lay the plan out in `buf` (host memory of at least L.total bytes).
@@ -265,6 +293,11 @@ void serialize(const pg_groups *g, const HostPlan &hp, const Layout &L, char *bu
   put(L.resp_start, hp.rstart);
   put(L.resp_len, hp.rlen);
   put(L.resp_group, hp.rgroup);
+  put(L.scored_row, hp.sc_row);
+  put(L.scored_pred, hp.sc_pred);
+  put(L.scored_resp, hp.sc_resp);
+  put(L.pred_start, hp.pred_start);
+  put(L.pred_list, hp.pred_list);
   if (pos_ids && hp.T > 0) std::memcpy(pos_ids, hp.pos.data(), size_t(hp.T) * 4);
   auto arr = [&](size_t off) { return reinterpret_cast<int32_t *>(buf + off); };
   int32_t *qa = arr(L.q_tiles), *ka = arr(L.kv_tiles), *ia = arr(L.kv_items);
@@ -304,6 +337,7 @@ void serialize(const pg_groups *g, const HostPlan &hp, const Layout &L, char *bu
   d.num_kv_sums = int32_t(hp.sums.size() / 4);
   d.num_kv_parts = hp.n_parts;
   d.total_prefix_rows = hp.pbefore[g->num_groups];
+  d.num_scored = int32_t(hp.sc_row.size());
   d.pairs = hp.pairs;
   d.baseline_pairs = hp.base_pairs;
   d.buf_bytes = L.total;
@@ -324,6 +358,11 @@ void point_into(pg_desc *d, const Layout &L, const char *base) {
   d->resp_start = p(L.resp_start);
   d->resp_len = p(L.resp_len);
   d->resp_group = p(L.resp_group);
+  d->scored_row = p(L.scored_row);
+  d->scored_pred = p(L.scored_pred);
+  d->scored_resp = p(L.scored_resp);
+  d->pred_start = p(L.pred_start);
+  d->pred_list = p(L.pred_list);
 }
 
 pg_status check_desc(const pg_desc *d) {
@@ -386,8 +425,8 @@ pg_status hip_status(hipError_t e, const char *what) {
 float resolve_scale(float s, int D) { return s > 0.f ? s : 1.0f / std::sqrt(float(D)); }
 
 // ---------------------------------------------------------------- kernel timing
-const char *const kKernelNames[PG_KERNEL_COUNT] = {"fwd",    "bwd_pre", "bwd_dkdv",
-                                                   "bwd_dq", "rope",    "rows"};
+const char *const kKernelNames[PG_KERNEL_COUNT] = {
+    "fwd", "bwd_pre", "bwd_dkdv", "bwd_dq", "rope", "rows", "head_fwd", "head_bwd", "grpo_loss"};
 
 struct TimedLaunch {
   int id;
@@ -503,6 +542,94 @@ pg_status rows_call(const pg_desc *d, bool pack, void *packed, void *pre, void *
   return hip_status(timed(PG_KERNEL_ROWS, s,
                           [&] { return pg::launch_rows(p, pack, packed, pre, resp, row_bytes, s); }),
                     pack ? "pg_pack_rows launch" : "pg_unpack_rows launch");
+}
+
+// ---------------------------------------------------------------- log-prob head
+// One rocBLAS handle per device, created on first use; the stream is set and
+// the GEMMs are enqueued under the lock.  Atomics are disallowed, so the
+// GEMMs are deterministic.
+struct Blas {
+  std::mutex mu;
+  std::map<int, rocblas_handle> handles;
+};
+Blas &blas() {
+  static Blas b;
+  return b;
+}
+
+pg_status blas_status(rocblas_status st, const char *what) {
+  if (st == rocblas_status_success) return PG_OK;
+  return fail(PG_ERR_HIP, std::string(what) + ": " + rocblas_status_to_string(st));
+}
+
+// Row-major products with bf16 operands and fp32 results, as rocBLAS
+// column-major calls (a row-major [r x c] matrix is a column-major [c x r]).
+rocblas_status gemm_bf16(rocblas_handle h, rocblas_operation ta, rocblas_operation tb, int m, int n,
+                         int k, const void *A, int lda, const void *B, int ldb, float *D, int ldd) {
+  const float one = 1.f, zero = 0.f;
+  return rocblas_gemm_ex(h, ta, tb, m, n, k, &one, A, rocblas_datatype_bf16_r, lda, B,
+                         rocblas_datatype_bf16_r, ldb, &zero, D, rocblas_datatype_f32_r, ldd, D,
+                         rocblas_datatype_f32_r, ldd, rocblas_datatype_f32_r,
+                         rocblas_gemm_algo_standard, 0, 0);
+}
+
+pg_status get_blas(Blas &b, rocblas_handle *out) {  // b.mu held
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  auto it = b.handles.find(dev);
+  if (it == b.handles.end()) {
+    rocblas_handle h = nullptr;
+    pg_status st = blas_status(rocblas_create_handle(&h), "rocblas_create_handle");
+    if (st != PG_OK) return st;
+    if ((st = blas_status(rocblas_set_atomics_mode(h, rocblas_atomics_not_allowed),
+                          "rocblas_set_atomics_mode")) != PG_OK)
+      return st;
+    it = b.handles.emplace(dev, h).first;
+  }
+  *out = it->second;
+  return PG_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Workspace of the head: logits Z [n, V] fp32, G [n, V] bf16, H_pred [n, dm]
+// bf16, dH_pred [n, dm] fp32.
+struct HeadWs {
+  size_t z, g, hp, dhp, total;
+};
+HeadWs head_ws(int64_t n, int64_t V, int64_t dm) {
+  HeadWs w{};
+  w.z = 0;
+  w.g = align256(w.z + size_t(n) * V * 4);
+  w.hp = align256(w.g + size_t(n) * V * 2);
+  w.dhp = align256(w.hp + size_t(n) * dm * 2);
+  w.total = std::max<size_t>(256, align256(w.dhp + size_t(n) * dm * 4));
+  return w;
+}
+
+pg_status check_head(const pg_desc *d, int32_t vocab, int32_t d_model) {
+  pg_status st = check_desc(d);
+  if (st != PG_OK) return st;
+  if (vocab < 1 || d_model < 8 || d_model % 8)
+    return fail(PG_ERR_INVALID_ARG, "vocab must be >= 1 and d_model a positive multiple of 8");
+  if (d->num_scored < 0 || d->num_resp < 0)
+    return fail(PG_ERR_INVALID_ARG, "descriptor is not one filled by pg_pack");
+  if (d->num_scored > 0 && (!d->scored_row || !d->scored_pred || !d->scored_resp ||
+                            !d->pred_start || !d->pred_list))
+    return fail(PG_ERR_INVALID_ARG, "descriptor arrays are NULL");
+  return PG_OK;
+}
+
+// The row-major products of the head, in rocBLAS terms:
+//   Z [n, V]  = H_pred [n, dm] W^T        -> (T, N): m = V,  n = n,  k = dm
+//   dH [n, dm] = G [n, V] W [V, dm]       -> (N, N): m = dm, n = n,  k = V
+//   dW [V, dm] = G^T H_pred               -> (N, T): m = dm, n = V,  k = n
+pg_status head_logits(rocblas_handle h, const void *hp, const void *weight, float *z, int n, int V,
+                      int dm) {
+  return blas_status(gemm_bf16(h, rocblas_operation_transpose, rocblas_operation_none, V, n, dm,
+                               weight, dm, hp, dm, z, V),
+                     "logits GEMM");
 }
 
 }  // namespace
@@ -659,6 +786,117 @@ pg_status pg_unpack_rows(const pg_desc *d, const void *packed_rows, void *prefix
                          void *resp_rows, size_t row_bytes, void *stream) {
   return rows_call(d, false, const_cast<void *>(packed_rows), prefix_rows, resp_rows, row_bytes,
                    stream);
+}
+
+size_t pg_logprob_workspace_size(const pg_desc *d, int32_t vocab, int32_t d_model) {
+  if (check_head(d, vocab, d_model) != PG_OK) return 0;
+  return head_ws(d->num_scored, vocab, d_model).total;
+}
+
+pg_status pg_logprob_fwd(const pg_desc *d, const void *hidden, const void *weight, int32_t vocab,
+                         int32_t d_model, const int32_t *tokens, float *logp, float *lse,
+                         void *workspace, size_t ws_bytes, void *stream) {
+  pg_status st = check_head(d, vocab, d_model);
+  if (st != PG_OK) return st;
+  const int n = d->num_scored;
+  if (n == 0) return PG_OK;
+  if ((st = check_ptrs({{hidden, "hidden"}, {weight, "weight"}, {tokens, "tokens"}, {logp, "logp"},
+                        {lse, "lse"}, {workspace, "workspace"}})) != PG_OK)
+    return st;
+  const HeadWs w = head_ws(n, vocab, d_model);
+  if (ws_bytes < w.total)
+    return fail(PG_ERR_WORKSPACE, "workspace too small: need " + std::to_string(w.total) +
+                                      " bytes, got " + std::to_string(ws_bytes));
+  char *ws = static_cast<char *>(workspace);
+  float *z = reinterpret_cast<float *>(ws + w.z);
+  void *hp = ws + w.hp;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Blas &b = blas();
+  std::lock_guard<std::mutex> lock(b.mu);
+  rocblas_handle h;
+  if ((st = get_blas(b, &h)) != PG_OK) return st;
+  if ((st = blas_status(rocblas_set_stream(h, s), "rocblas_set_stream")) != PG_OK) return st;
+  pg_status gst = PG_OK;
+  hipError_t e = timed(PG_KERNEL_HEAD_FWD, s, [&] {
+    hipError_t r = pg::launch_gather_rows(d->scored_pred, hidden, hp, n, d_model, s);
+    if (r != hipSuccess) return r;
+    if ((gst = head_logits(h, hp, weight, z, n, vocab, d_model)) != PG_OK) return hipErrorUnknown;
+    return pg::launch_lsm_fwd(z, d->scored_row, tokens, logp, lse, n, vocab, s);
+  });
+  if (gst != PG_OK) return gst;
+  return hip_status(e, "pg_logprob_fwd launch");
+}
+
+pg_status pg_grpo_loss(const pg_desc *d, const float *logp, const float *advantages, float *loss,
+                       float *dlogp, void *stream) {
+  pg_status st = check_desc(d);
+  if (st != PG_OK) return st;
+  if (d->num_scored > 0 && !d->scored_resp)
+    return fail(PG_ERR_INVALID_ARG, "descriptor arrays are NULL");
+  if (d->num_resp == 0) return fail(PG_ERR_INVALID_ARG, "the batch has no responses");
+  if ((st = check_ptrs({{advantages, "advantages"}, {loss, "loss"}})) != PG_OK) return st;
+  if (d->num_scored > 0 && (st = check_ptrs({{logp, "logp"}, {dlogp, "dlogp"}})) != PG_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return hip_status(timed(PG_KERNEL_LOSS, s, [&] {
+                      return pg::launch_grpo_loss(logp, d->scored_resp, advantages, loss, dlogp,
+                                                  d->num_scored, d->num_resp, s);
+                    }),
+                    "pg_grpo_loss launch");
+}
+
+pg_status pg_logprob_bwd(const pg_desc *d, const void *hidden, const void *weight, int32_t vocab,
+                         int32_t d_model, const int32_t *tokens, const float *lse,
+                         const float *dlogp, float *dhidden, float *dweight, void *workspace,
+                         size_t ws_bytes, void *stream) {
+  pg_status st = check_head(d, vocab, d_model);
+  if (st != PG_OK) return st;
+  const int n = d->num_scored;
+  if ((st = check_ptrs({{hidden, "hidden"}, {weight, "weight"}, {dweight, "dweight"},
+                        {workspace, "workspace"}})) != PG_OK)
+    return st;
+  if (d->total_rows > 0 && (st = check_ptrs({{dhidden, "dhidden"}})) != PG_OK) return st;
+  if (n > 0 && (st = check_ptrs({{tokens, "tokens"}, {lse, "lse"}, {dlogp, "dlogp"}})) != PG_OK)
+    return st;
+  const HeadWs w = head_ws(n, vocab, d_model);
+  if (ws_bytes < w.total)
+    return fail(PG_ERR_WORKSPACE, "workspace too small: need " + std::to_string(w.total) +
+                                      " bytes, got " + std::to_string(ws_bytes));
+  char *ws = static_cast<char *>(workspace);
+  float *z = reinterpret_cast<float *>(ws + w.z);
+  void *g = ws + w.g;
+  void *hp = ws + w.hp;
+  float *dhp = reinterpret_cast<float *>(ws + w.dhp);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Blas &b = blas();
+  std::lock_guard<std::mutex> lock(b.mu);
+  rocblas_handle h;
+  if ((st = get_blas(b, &h)) != PG_OK) return st;
+  if ((st = blas_status(rocblas_set_stream(h, s), "rocblas_set_stream")) != PG_OK) return st;
+  pg_status gst = PG_OK;
+  hipError_t e = timed(PG_KERNEL_HEAD_BWD, s, [&] {
+    hipError_t r = hipSuccess;
+    if (n > 0) {
+      if ((r = pg::launch_gather_rows(d->scored_pred, hidden, hp, n, d_model, s)) != hipSuccess)
+        return r;
+      if ((gst = head_logits(h, hp, weight, z, n, vocab, d_model)) != PG_OK) return hipErrorUnknown;
+      if ((r = pg::launch_lsm_bwd(z, d->scored_row, tokens, lse, dlogp, g, n, vocab, s)) !=
+          hipSuccess)
+        return r;
+      if ((gst = blas_status(gemm_bf16(h, rocblas_operation_none, rocblas_operation_none, d_model,
+                                       n, vocab, weight, d_model, g, vocab, dhp, d_model),
+                             "dhidden GEMM")) != PG_OK)
+        return hipErrorUnknown;
+    }
+    // dW = G^T H_pred (zeros when nothing is scored: k = 0, beta = 0)
+    if ((gst = blas_status(gemm_bf16(h, rocblas_operation_none, rocblas_operation_transpose,
+                                     d_model, vocab, n, hp, d_model, g, vocab, dweight, d_model),
+                           "dweight GEMM")) != PG_OK)
+      return hipErrorUnknown;
+    return pg::launch_scatter_rows(d->pred_start, d->pred_list, dhp, dhidden, d->total_rows,
+                                   d_model, s);
+  });
+  if (gst != PG_OK) return gst;
+  return hip_status(e, "pg_logprob_bwd launch");
 }
 
 pg_status pg_kernel_timing(int32_t enable) {

@@ -59,6 +59,20 @@ hipError_t launch_bwd_dq_f32(const Plan &p, float scale, const void *q, const vo
 hipError_t launch_rows(const Plan &p, bool pack, void *packed, void *pre, void *resp,
                        size_t row_bytes, hipStream_t s);
 
+// Log-probability head kernels (the GEMMs around them are rocBLAS calls).
+hipError_t launch_gather_rows(const int32_t *pred, const void *hidden, void *out, int n,
+                              int d_model, hipStream_t s);
+hipError_t launch_lsm_fwd(const float *z, const int32_t *scored_row, const int32_t *tokens,
+                          float *logp, float *lse, int n, int V, hipStream_t s);
+hipError_t launch_grpo_loss(const float *logp, const int32_t *scored_resp, const float *adv,
+                            float *loss, float *dlogp, int n, int n_resp, hipStream_t s);
+hipError_t launch_lsm_bwd(const float *z, const int32_t *scored_row, const int32_t *tokens,
+                          const float *lse, const float *dlogp, void *g, int n, int V,
+                          hipStream_t s);
+hipError_t launch_scatter_rows(const int32_t *pred_start, const int32_t *pred_list,
+                               const float *dh_pred, float *dhidden, int T, int d_model,
+                               hipStream_t s);
+
 // Rotary embedding in place.
 hipError_t launch_rope(int T, int H, int D, pg_dtype t, void *x, const int32_t *pos,
                        float theta, int inverse, hipStream_t s);

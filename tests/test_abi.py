@@ -319,6 +319,33 @@ def test_row_gather_plan_and_validation():
     assert no_pre.total_prefix_rows == 0 and no_pre.total_rows == 3
 
 
+def test_head_sizes_and_validation():
+    """Log-probability head: workspace size from the descriptor, and bad
+    arguments rejected on the host before anything is enqueued."""
+    L = _lib()
+    desc, buf = _host_desc(((5, [3, 0, 4]), (0, [2, 1]), (1, [1])))
+    assert desc.num_scored == 9
+    n, V, dm = 9, 1000, 64
+    a256 = lambda x: -(-x // 256) * 256
+    z = n * V * 4
+    g = a256(z) + n * V * 2
+    hp = a256(g) + n * dm * 2
+    want = a256(a256(hp) + n * dm * 4)
+    assert L.pg_logprob_workspace_size(ctypes.byref(desc), V, dm) == want
+    assert L.pg_logprob_workspace_size(ctypes.byref(desc), 0, dm) == 0
+    assert L.pg_logprob_workspace_size(ctypes.byref(desc), V, 12) == 0
+    p = ctypes.c_void_p(4096)
+    assert L.pg_logprob_fwd(ctypes.byref(desc), p, p, V, dm, p, p, p, p, want - 1,
+                            None) == pg.PG_ERR_WORKSPACE
+    assert L.pg_logprob_fwd(ctypes.byref(desc), None, p, V, dm, p, p, p, p, want,
+                            None) == pg.PG_ERR_INVALID_ARG
+    assert "hidden" in L.pg_last_error().decode()
+    assert L.pg_logprob_bwd(ctypes.byref(desc), p, p, V, dm, p, p, p, p, None, p, want,
+                            None) == pg.PG_ERR_INVALID_ARG
+    assert "dweight" in L.pg_last_error().decode()
+    assert L.pg_grpo_loss(ctypes.byref(desc), p, None, p, p, None) == pg.PG_ERR_INVALID_ARG
+
+
 def test_python_binding_has_no_fallback():
     """The binding imports neither the oracle nor any CPU path."""
     src = open(pg.__file__).read()

@@ -9,7 +9,7 @@ import pytest
 
 from oracle.attention import member_sequences
 from oracle.logprob import (advantages_from_rewards, baseline_logprob_grads, baseline_logprobs,
-                            grpo_loss, scored_rows)
+                            grpo_loss, sampled_head, scored_rows)
 
 torch = pytest.importorskip("torch")
 
@@ -170,3 +170,17 @@ def test_grpo_gradients_match_autograd():
     assert abs(float(tloss.detach()) - loss) < 1e-12
     np.testing.assert_allclose(g["dhidden"], h.grad.numpy(), atol=1e-12)
     np.testing.assert_allclose(g["dW"], w.grad.numpy(), atol=1e-12)
+
+
+def test_sampled_head_matches_full_oracle():
+    hidden, W, tokens = _inputs(GROUPS, V=9, dm=5, seed=10)
+    tgt, _ = scored_rows(GROUPS)
+    dl = np.random.default_rng(11).standard_normal(tgt.size)
+    full = baseline_logprobs(GROUPS, hidden, W, tokens)
+    g = baseline_logprob_grads(GROUPS, hidden, W, tokens, dl)
+    ks, hs, vs = [0, 3, 7, 8], [4, 5, 12, 15, 0, 16], [0, 4, 8]
+    s = sampled_head(GROUPS, hidden, W, tokens, dl, ks, hs, vs, row_block=2)
+    np.testing.assert_allclose(s["logp"], full["logp"][ks], atol=1e-12)
+    np.testing.assert_allclose(s["lse"], full["lse"][ks], atol=1e-12)
+    np.testing.assert_allclose(s["dhidden"], g["dhidden"][hs], atol=1e-12)
+    np.testing.assert_allclose(s["dW"], g["dW"][vs], atol=1e-12)
