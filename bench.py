@@ -2,7 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--no-baseline] [--no-cpu] [--cpu-seconds S] [--forward-only]
-                    [--ratio-sweep] [--pack-rows]
+                    [--ratio-sweep] [--pack-rows] [--grpo-head]
 
 One step is one pass of the whole path over one packed batch with inputs
 already resident in HBM: pg_pack (plan + descriptor upload), pg_attn_fwd and
@@ -14,6 +14,10 @@ pg_attn_bwd.  Prints ONE JSON line on stdout; progress goes to stderr.
            repeated-prefix layout (same kernels), their ratio beside the exact
            attention-FLOP ratio pairs_g / pairs_b and its limit 1/G, and the
            bytes of the path's tensors in each layout.  One JSON line.
+--grpo-head  the response log-probability head of the GRPO step (logits of
+           the scored rows, log-softmax + gather, policy loss, backward) on
+           the head workload (P = 8192, 16 responses, d_model 2048, vocab
+           32000); value credits 6 * N * V * d_model flops per step.
 --pack-rows  pg_pack_rows gathering the workload's [T, Hq, d] bf16 rows from a
            prefix buffer and a response buffer into packed order; value in
            GB/s (read + write) against 8 TB/s of HBM.  One JSON line.
@@ -74,6 +78,8 @@ def parse(argv=None):
                     help="time grouped vs repeated-prefix layouts over prefix/response ratios")
     ap.add_argument("--forward-only", action="store_true",
                     help="score without backward and without storing the logsumexp")
+    ap.add_argument("--grpo-head", action="store_true",
+                    help="time the response log-probability head of the GRPO step (fwd, loss, bwd)")
     ap.add_argument("--pack-rows", action="store_true",
                     help="time pg_pack_rows gathering the workload's [T, Hq, d] rows into packed order")
     ap.add_argument("--no-baseline", action="store_true", help="skip the repeated-prefix run")
@@ -291,6 +297,67 @@ def pack_rows_bench(a, pg, torch, w) -> dict:
                          "frac": round(gbs / 8000.0, 4), "traffic": None}}
 
 
+def grpo_head_bench(a, pg, torch) -> dict:
+    """One step of the GRPO log-probability head on the head workload: pg_pack,
+    pg_logprob_fwd, pg_grpo_loss, pg_logprob_bwd.  Credited 6 * N * V * d_model
+    flops (logits, dhidden and dweight products once each; the backward's
+    recomputation of the logits is not credited), N = scored response rows."""
+    from workloads import draw_head_inputs, head_workloads
+    w = head_workloads()["grpo_head_g16_p8192"]
+    groups = groups_of(w)
+    arrs = draw_head_inputs(w)
+    dev = "cuda"
+    h = torch.from_numpy(arrs["hidden"]).to(dev).to(torch.bfloat16)
+    W = torch.from_numpy(arrs["weight"]).to(dev).to(torch.bfloat16)
+    tok = torch.from_numpy(arrs["tokens"]).to(dev)
+    r = arrs["rewards"].astype(np.float64)
+    adv = torch.from_numpy((r - r.mean()).astype(np.float32)).to(dev)  # the page's baseline variant
+    batch = pg.pg_pack(groups, 1, 1, 64)
+    n = batch.desc.num_scored
+    need = pg.lib().pg_logprob_workspace_size(ctypes.byref(batch.desc), w.vocab, w.d_model)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+
+    def step():
+        b = pg.pg_pack(groups, 1, 1, 64)
+        logp, lse = pg.pg_logprob_fwd(b, h, W, tok, workspace=ws)
+        loss, dlogp = pg.pg_grpo_loss(b, logp, adv)
+        return pg.pg_logprob_bwd(b, h, W, tok, lse, dlogp, workspace=ws)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    pg.pg_kernel_timing(True)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(a.steps):
+        step()
+    stop.record()
+    torch.cuda.synchronize()
+    kt = pg.pg_kernel_times()
+    pg.pg_kernel_timing(False)
+    ms = start.elapsed_time(stop) / a.steps
+    flops = 6.0 * n * w.vocab * w.d_model
+    tf = flops / (ms * 1e-3) / 1e12
+    (nb, tb), (nf, tfw) = kt["head_bwd"], kt["head_fwd"]
+    bwd_ms = tb / nb
+    bwd_tf = 6.0 * n * w.vocab * w.d_model / (bwd_ms * 1e-3) / 1e12  # recompute + 2 products
+    rows_all = w.total_rows
+    rows_rep = sum(g.prefix_len * len(g.resp_lens) + sum(g.resp_lens) for g in w.groups)
+    log(f"[bench] grpo head: {ms:.3f} ms/step, {tf:.1f} TFLOP/s; fwd {tfw / nf:.3f} ms, bwd {bwd_ms:.3f} ms, "
+        f"loss {kt['grpo_loss'][1] / max(1, kt['grpo_loss'][0]):.4f} ms; scored rows {n} of {rows_all} "
+        f"packed, {rows_rep} in the repeated-prefix layout")
+    return {"metric": "GRPO response log-prob head fwd+bwd TFLOP/s", "value": round(tf, 1),
+            "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+            "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1) hidden states, "
+            "N(0,0.02^2) head, uniform token ids, N(0,1) rewards)",
+            "config": {"workload": w.name, "scored_rows": n, "d_model": w.d_model, "vocab": w.vocab,
+                       "packed_rows": rows_all, "repeated_prefix_rows": rows_rep},
+            "roofline": {"bound": "mfma", "kernel": "head_bwd", "achieved": round(bwd_tf, 1),
+                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(bwd_tf / PEAK_BF16_TFLOPS, 4),
+                         "traffic": None}}
+
+
 def main(argv=None) -> int:
     a = parse(argv)
     if a.gpus != 1:
@@ -312,6 +379,9 @@ def main(argv=None) -> int:
     w = attention_workloads()[a.workload or ("bf16_scoring_p32768" if fwd_only else "bf16_gqa_g16_p8192")]
     if a.pack_rows:
         print(json.dumps(pack_rows_bench(a, pg, torch, w)), flush=True)
+        return 0
+    if a.grpo_head:
+        print(json.dumps(grpo_head_bench(a, pg, torch)), flush=True)
         return 0
     groups = groups_of(w)
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32

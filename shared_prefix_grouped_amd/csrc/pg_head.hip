@@ -12,8 +12,8 @@
 //   gather_rows   H_pred[k] = hidden[pred[k]]
 //   lsm_fwd       per scored row: logsumexp over the vocabulary (one pass,
 //                 running max) and logp = z[token] - lse
-//   grpo_loss     per response: sum of its logp; loss = -mean(A_i * S_i);
-//                 dlogp[k] = -A_{resp(k)} / n_resp
+//   grpo_loss     loss = -mean_i(A_i * S_i), S_i = sum of response i's logp,
+//                 summed entry by entry; dlogp[k] = -A_{resp(k)} / n_resp
 //   lsm_bwd       G[k, v] = dlogp[k] * ([v == token] - exp(z[k, v] - lse[k]))
 //   scatter_rows  dhidden[t] = sum of dH_pred[k] over the entries t predicts,
 //                 in entry order (the last prefix row of a group sums its G
@@ -91,23 +91,14 @@ __global__ __launch_bounds__(kHeadThreads) void lsm_fwd_kernel(
   }
 }
 
-// One block: S_r = sum of the response's logp (its scored entries are
-// contiguous: scored_resp is non-decreasing), loss = -mean(A_r * S_r).
+// One block: loss = -(1/n_resp) sum_r A_r S_r = -(1/n_resp) sum_k A_{resp(k)} logp_k,
+// each thread taking entries k = tid, tid + 256, ... and a fixed tree after.
 __global__ __launch_bounds__(kHeadThreads) void grpo_loss_kernel(
     const float *__restrict__ logp, const int32_t *__restrict__ scored_resp,
     const float *__restrict__ adv, float *__restrict__ loss, int n, int n_resp) {
   __shared__ float part[kHeadThreads];
   float acc = 0.f;
-  for (int r = threadIdx.x; r < n_resp; r += kHeadThreads) {
-    int lo = 0, hi = n;  // first entry of response r
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (scored_resp[mid] < r) lo = mid + 1; else hi = mid;
-    }
-    float s = 0.f;
-    for (int k = lo; k < n && scored_resp[k] == r; ++k) s += logp[k];
-    acc += adv[r] * s;
-  }
+  for (int k = threadIdx.x; k < n; k += kHeadThreads) acc += adv[scored_resp[k]] * logp[k];
   part[threadIdx.x] = acc;
   __syncthreads();
   for (int w = kHeadThreads / 2; w > 0; w >>= 1) {
