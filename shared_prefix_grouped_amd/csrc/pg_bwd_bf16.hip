@@ -59,18 +59,19 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const Tin *__restrict__ O,
 
 // ---------------------------------------------------------------- dK, dV
 // A workgroup owns 128 key rows of one kv head, as 4 groups of 32 keys, and
-// runs 8 waves: for each key group, wave A computes S = Q K^T, P and
-// dV^T += dO^T P, and wave B computes dP = dO V^T, dS = P * (dP - delta) and
-// dK^T += Q^T dS, receiving P (fp32) from wave A through LDS.  Each wave then
-// holds one accumulator set and one K or V operand set, so two waves fit on
-// a SIMD and one's softmax arithmetic overlaps the other's matrix work.
+// runs 8 waves, two per key group.  Wave A holds the group's K and V rows and
+// computes, per 32-row query block, S = Q K^T and dP = dO V^T, then
+// P = exp(S - LSE) and dS = P * (dP - delta); it publishes P and dS, packed to
+// bf16 in the MFMA operand layout, in LDS.  Wave B holds the dV^T and dK^T
+// accumulators and adds dV^T += dO^T P and dK^T += Q^T dS.  Each role then
+// issues 16 MFMAs per step, and B, free of operand registers, can keep its
+// fragment reads in flight.
 //
 // The query rows are walked in steps of 32 (one MFMA block) with one barrier
-// per step: in step n wave A forms P_n, publishes it in LDS and adds block n
-// into dV; wave B forms dS_{n-1} (P_{n-1} was published by the barrier that
-// opened step n), adds it into dK, and computes dP_n, which it keeps in
-// registers for the next step.  Q/dO rows (+ LSE, delta) live in a ring of
-// NSLOT LDS slots, staged through registers (see stage / commit below).
+// per step: in step n wave A forms P_n and dS_n; wave B consumes P_{n-1} and
+// dS_{n-1} (published by the barrier that opened step n).  Q/dO rows (+ LSE,
+// delta) live in a ring of NSLOT LDS slots, staged through registers of the
+// A waves (see stage / commit below).
 template <int D>
 struct DkdvCfg {
   static constexpr int BN = PG_TILE_KV;  // key rows per workgroup
@@ -96,9 +97,9 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
   __shared__ __attribute__((aligned(16))) bf16 sdO[C::NSLOT * C::BM * D];
   __shared__ __attribute__((aligned(16))) float sL[C::NSLOT * 64];
   __shared__ __attribute__((aligned(16))) float sDl[C::NSLOT * 64];
-  // P of one 32x32 block per key group, by step parity, in the accumulator
-  // layout: [group][parity][register quad][lane].
-  __shared__ __attribute__((aligned(16))) f32x4 sP[C::NG][2][4][64];
+  // P and dS of one 32x32 block per key group, by step parity, as bf16 MFMA
+  // B operands: [group][parity][P0, P1, dS0, dS1][lane].
+  __shared__ __attribute__((aligned(16))) bf16x8 sX[C::NG][2][4][64];
 
   int item, hk;
   xcd_kvhead_work(blockIdx.x, Hkv, item, hk);
@@ -130,25 +131,30 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
   SwzFrags<D> frag;
   frag.init(lane);
 
-  // K (role A) or V (role B) rows of the group as MFMA B operands:
-  // column = key l32, k = d.  The resource spans rows [kw0, k1), so keys
-  // past the tile read as zero; the head offset rides in the scalar offset.
-  bf16x8 kvf[D / 16];
-  {
+  // K and V rows of the group (role A) as MFMA B operands: column = key
+  // l32, k = d.  The resources span rows [kw0, k1), so keys past the tile
+  // read as zero; the head offset rides in the scalar offset.
+  bf16x8 kf[D / 16], vf[D / 16];
+  if (roleA) {
     const size_t kv_row = (size_t)Hkv * D * sizeof(bf16);
-    const __amdgpu_buffer_rsrc_t rKV = buffer_resource(
-        (roleA ? K : V) + (size_t)kw0 * Hkv * D, group_active ? (size_t)(k1 - kw0) * kv_row : 0);
+    const size_t span = group_active ? (size_t)(k1 - kw0) * kv_row : 0;
+    const __amdgpu_buffer_rsrc_t rK = buffer_resource(K + (size_t)kw0 * Hkv * D, span);
+    const __amdgpu_buffer_rsrc_t rV = buffer_resource(V + (size_t)kw0 * Hkv * D, span);
     const int voff = l32 * (int)kv_row + 16 * hi;
 #pragma unroll
-    for (int st = 0; st < D / 16; ++st)
-      kvf[st] = __builtin_bit_cast(
-          bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rKV, voff + 32 * st, hk * D * 2, 0));
+    for (int st = 0; st < D / 16; ++st) {
+      kf[st] = __builtin_bit_cast(
+          bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rK, voff + 32 * st, hk * D * 2, 0));
+      vf[st] = __builtin_bit_cast(
+          bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rV, voff + 32 * st, hk * D * 2, 0));
+    }
   }
   // Let these loads complete here: left to the compiler, the wait for them
   // lands at their first use inside the step loop, where it would also wait
   // for the prefetch copies issued in the same step.
   wait_async_loads();
-  pin(kvf);
+  pin(kf);
+  pin(vf);
 
   // dK^T and dV^T (role B): register r of lane l holds d = 32 nb +
   // mfma_row(r, hi), key = l32.
@@ -273,7 +279,7 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
   pin(sto);
   pin(stl);
   if (roleA) {
-    // S -> P for step n; P (fp32) goes to LDS for wave B, which uses it in
+    // S, dP -> P, dS for step n, published for wave B, which uses them in
     // step n+1.  The loop runs to n = nS so that every wave meets the same
     // barriers.
     Step cur = first;
@@ -287,19 +293,27 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
       advance(cur);
       if (n < nS && block_live(c0)) {
         lds_cchar *cQ = slot_q(k);
+        lds_cchar *cdO = slot_do(k);
         const float *cL = sL + k * 64;
-        f32x16 s;
+        const float *cDl = sDl + k * 64;
+        f32x16 sc, dp;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[r] = 0.f;
+        for (int r = 0; r < 16; ++r) {
+          sc[r] = 0.f;
+          dp[r] = 0.f;
+        }
 #pragma unroll
-        for (int st = 0; st < D / 16; ++st) s = mfma32(frag.row(cQ, 0, st), kvf[st], s);
+        for (int st = 0; st < D / 16; ++st) {
+          sc = mfma32(frag.row(cQ, 0, st), kf[st], sc);
+          dp = mfma32(frag.row(cdO, 0, st), vf[st], dp);
+        }
         f32x16 p;
 #pragma unroll
         for (int rq = 0; rq < 4; ++rq) {
           const f32x4 Lq = *reinterpret_cast<const f32x4 *>(&cL[rq * 8 + hi * 4]);
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            p[rq * 4 + j] = fast_exp2(fmaf(s[rq * 4 + j], scale_log2, -Lq[j]));
+            p[rq * 4 + j] = fast_exp2(fmaf(sc[rq * 4 + j], scale_log2, -Lq[j]));
         }
         if (!block_full(c0)) {
           // query row c0 + 8 rq + 4 hi + j sees this key iff its distance
@@ -315,13 +329,17 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
             for (int j = 0; j < 4; ++j)
               p[rq * 4 + j] = (unsigned)(dq0 + rq * 8 + j) < span ? p[rq * 4 + j] : 0.f;
         }
+        // dS = P * (dP - delta)
 #pragma unroll
         for (int rq = 0; rq < 4; ++rq) {
-          f32x4 pq;
+          const f32x4 Dq = *reinterpret_cast<const f32x4 *>(&cDl[rq * 8 + hi * 4]);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) pq[j] = p[rq * 4 + j];
-          sP[kg][k & 1][rq][lane] = pq;
+          for (int j = 0; j < 4; ++j) dp[rq * 4 + j] = p[rq * 4 + j] * (dp[rq * 4 + j] - Dq[j]);
         }
+        sX[kg][k & 1][0][lane] = pack8(p, 0);
+        sX[kg][k & 1][1][lane] = pack8(p, 8);
+        sX[kg][k & 1][2][lane] = pack8(dp, 0);
+        sX[kg][k & 1][3][lane] = pack8(dp, 8);
       }
     }
   } else {
@@ -330,7 +348,6 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
     // that loop's copies in and wait for them (and so for this step's own
     // copies) in the middle of every step.
     wait_async_loads();
-    f32x16 dp;  // dP of the previous step
     bool live_prev = false;
     Step cur = first;
     for (int n0 = 0; n0 <= nS; n0 += C::NSLOT)
@@ -344,48 +361,21 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
       const bool live = n < nS && block_live(c0);
       const int kp = (k + C::NSLOT - 1) & (C::NSLOT - 1);  // slot of step n-1
       if (live_prev) {
-        // dV^T += dO_{n-1}^T P_{n-1}; dS_{n-1} = P_{n-1} * (dP_{n-1} - delta),
-        // dK^T += Q_{n-1}^T dS_{n-1}
+        // dV^T += dO_{n-1}^T P_{n-1}, dK^T += Q_{n-1}^T dS_{n-1}
         lds_cchar *cQ = slot_q(kp);
         lds_cchar *cdO = slot_do(kp);
-        const float *cDl = sDl + kp * 64;
-        f32x16 p;
+        const bf16x8 p0 = sX[kg][kp & 1][0][lane], p1 = sX[kg][kp & 1][1][lane];
+        const bf16x8 d0 = sX[kg][kp & 1][2][lane], d1 = sX[kg][kp & 1][3][lane];
 #pragma unroll
-        for (int rq = 0; rq < 4; ++rq) {
-          const f32x4 pq = sP[kg][kp & 1][rq][lane];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) p[rq * 4 + j] = pq[j];
+        for (int nb = 0; nb < D / 32; ++nb) {
+          accv[nb] = mfma32(frag.tr(cdO, 0, nb), p0, accv[nb]);
+          acck[nb] = mfma32(frag.tr(cQ, 0, nb), d0, acck[nb]);
         }
 #pragma unroll
-        for (int sub = 0; sub < 2; ++sub) {
-          const bf16x8 pb = pack8(p, sub * 8);
-#pragma unroll
-          for (int nb = 0; nb < D / 32; ++nb)
-            accv[nb] = mfma32(frag.tr(cdO, sub * 16, nb), pb, accv[nb]);
+        for (int nb = 0; nb < D / 32; ++nb) {
+          accv[nb] = mfma32(frag.tr(cdO, 16, nb), p1, accv[nb]);
+          acck[nb] = mfma32(frag.tr(cQ, 16, nb), d1, acck[nb]);
         }
-#pragma unroll
-        for (int rq = 0; rq < 4; ++rq) {
-          const int ql = rq * 8 + hi * 4;
-          const f32x4 Dq = *reinterpret_cast<const f32x4 *>(&cDl[ql]);
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            dp[rq * 4 + j] = p[rq * 4 + j] * (dp[rq * 4 + j] - Dq[j]);
-        }
-#pragma unroll
-        for (int sub = 0; sub < 2; ++sub) {
-          const bf16x8 db = pack8(dp, sub * 8);
-#pragma unroll
-          for (int nb = 0; nb < D / 32; ++nb)
-            acck[nb] = mfma32(frag.tr(cQ, sub * 16, nb), db, acck[nb]);
-        }
-      }
-      if (live) {
-        // dP_n = dO_n V^T
-        lds_cchar *cdO = slot_do(k);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) dp[r] = 0.f;
-#pragma unroll
-        for (int st = 0; st < D / 16; ++st) dp = mfma32(frag.row(cdO, 0, st), kvf[st], dp);
       }
       live_prev = live;
     }
