@@ -31,6 +31,8 @@ struct FwdCfg {
   static constexpr int NW = BM / 32;    // waves
   static constexpr int NT = NW * 64;    // threads
   static constexpr int BN = 64;         // keys per chunk
+  static constexpr int NB = BN / 32;    // 32-key MFMA blocks per chunk
+  static constexpr int OCC = 2;         // workgroups per CU (LDS: 4 * BN * D * 2 bytes each)
 };
 
 // A row keeps a stale running max until a chunk raises it by more than
@@ -40,7 +42,7 @@ struct FwdCfg {
 constexpr float kRescale = 8.0f;
 
 template <int D>
-__global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
+__global__ __launch_bounds__(256, FwdCfg<D>::OCC) void fwd_bf16_kernel(
     const int32_t *__restrict__ q_tiles, const int32_t *__restrict__ row_lo,
     const bf16 *__restrict__ Q, const bf16 *__restrict__ K, const bf16 *__restrict__ V,
     bf16 *__restrict__ O, float *__restrict__ LSE, int T, int Hq, int Hkv, float scale_log2) {
@@ -149,19 +151,19 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
                       (c0 + C::BN <= pe || c0 >= lo_last);
 
     // S^T = K Q^T for two 32-key blocks
-    f32x16 s[2];
+    f32x16 s[C::NB];
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < C::NB; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[b][r] = 0.f;
     // both key blocks per k-step: consecutive MFMAs are independent
 #pragma unroll
     for (int st = 0; st < D / 16; ++st)
 #pragma unroll
-      for (int b = 0; b < 2; ++b) s[b] = mfma32(frag.row(cK, b * 32, st), qf[st], s[b]);
+      for (int b = 0; b < C::NB; ++b) s[b] = mfma32(frag.row(cK, b * 32, st), qf[st], s[b]);
     if (!full) {
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
+      for (int b = 0; b < C::NB; ++b)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = c0 + b * 32 + mfma_row(r, hi);
@@ -171,7 +173,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
     }
     float mx = s[0][0];
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < C::NB; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[b][r]);
     mx = fmaxf(mx, wave_swap_halves(mx)) * scale_log2;
@@ -188,7 +190,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
     const float neg_m = -m;
     float rs = 0.f;
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < C::NB; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float p = fast_exp2(fmaf(s[b][r], scale_log2, neg_m));
@@ -198,7 +200,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
     l += rs;
     // O^T += V^T P^T: A = V^T read transposed from row-major LDS, B = P^T from registers
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < C::NB; ++b)
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub) {
         const bf16x8 pf = pack8(s[b], sub * 8);
