@@ -2,7 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--no-baseline] [--no-cpu] [--cpu-seconds S] [--forward-only]
-                    [--ratio-sweep] [--pack-rows] [--grpo-head]
+                    [--ratio-sweep] [--pack-rows] [--grpo-head] [--decoder]
 
 One step is one pass of the whole path over one packed batch with inputs
 already resident in HBM: pg_pack (plan + descriptor upload), pg_attn_fwd and
@@ -14,6 +14,9 @@ pg_attn_bwd.  Prints ONE JSON line on stdout; progress goes to stderr.
            repeated-prefix layout (same kernels), their ratio beside the exact
            attention-FLOP ratio pairs_g / pairs_b and its limit 1/G, and the
            bytes of the path's tensors in each layout.  One JSON line.
+--decoder  the 4-layer decoder harness (fwd + bwd) on the packed rows and on the
+           repeated-prefix layout; value = credited model TFLOP/s on the
+           packed layout, with the speedup beside the flop ratio.
 --grpo-head  the response log-probability head of the GRPO step (logits of
            the scored rows, log-softmax + gather, policy loss, backward) on
            the head workload (P = 8192, 16 responses, d_model 2048, vocab
@@ -53,6 +56,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3     # MI355X dense fp32
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
@@ -78,6 +82,8 @@ def parse(argv=None):
                     help="time grouped vs repeated-prefix layouts over prefix/response ratios")
     ap.add_argument("--forward-only", action="store_true",
                     help="score without backward and without storing the logsumexp")
+    ap.add_argument("--decoder", action="store_true",
+                    help="time the 4-layer decoder harness (fwd+bwd) on the packed and the repeated-prefix layouts")
     ap.add_argument("--grpo-head", action="store_true",
                     help="time the response log-probability head of the GRPO step (fwd, loss, bwd)")
     ap.add_argument("--pack-rows", action="store_true",
@@ -317,6 +323,89 @@ def pack_rows_bench(a, pg, torch, w) -> dict:
                          "frac": round(gbs / 8000.0, 4), "traffic": None}}
 
 
+def decoder_bench(a, pg, torch) -> dict:
+    """The 4-layer decoder harness (fwd + bwd through every layer, grouped
+    attention and RoPE at baseline ids from this library, the rest PyTorch) on
+    the packed rows, and the same harness on the repeated-prefix layout (each
+    [P; R_i] its own group, prefix rows replicated).  Credited flops: per row
+    and layer 3 * (8 D^2 + 6 D F) for the projections and MLP (fwd + bwd), and
+    14 * d * H * pairs for attention, on the grouped layout."""
+    from shared_prefix_grouped_amd.decoder import DecoderConfig, decoder_forward, make_parameters
+    from workloads import decoder_workload, draw_decoder_inputs
+    w = decoder_workload()
+    arrs = draw_decoder_inputs(w)
+    cfg = DecoderConfig(w.num_layers, w.d_model, w.num_heads, w.ffn_dim, w.rope_theta, w.rms_eps)
+    groups = groups_of(w)
+    p = make_parameters(arrs, cfg)
+
+    def timed(groups_, x_np, dy_np, steps, warmup):
+        batch = pg.pg_pack(groups_, w.num_heads, w.num_heads, w.head_dim)
+        x = torch.from_numpy(x_np).cuda().requires_grad_(True)
+        dy = torch.from_numpy(dy_np).cuda()
+
+        def step():
+            for t in [x] + [t for n in p for t in (p[n] if isinstance(p[n], list) else [p[n]])]:
+                t.grad = None
+            decoder_forward(x, p, batch, cfg).backward(dy)
+
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        pg.pg_kernel_timing(True)
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record()
+        for _ in range(steps):
+            step()
+        s1.record()
+        torch.cuda.synchronize()
+        kt = pg.pg_kernel_times()
+        pg.pg_kernel_timing(False)
+        lib_ms = sum(t for n, (c, t) in kt.items()) / steps
+        return s0.elapsed_time(s1) / steps, lib_ms, batch
+
+    steps = max(2, a.steps // 4)
+    g_ms, g_lib, batch = timed(groups, arrs["x"], arrs["dy"], steps, 2)
+    idx = []
+    t = 0
+    for g in w.groups:
+        r0 = t + g.prefix_len
+        for r in g.resp_lens:
+            idx += list(range(t, t + g.prefix_len)) + list(range(r0, r0 + r))
+            r0 += r
+        t += g.rows
+    idx = np.asarray(idx)
+    rep_groups = [(g.prefix_len, [r]) for g in w.groups for r in g.resp_lens]
+    dy_rep = arrs["dy"][idx].copy()
+    b_ms, b_lib, bbatch = timed(rep_groups, arrs["x"][idx].copy(), dy_rep, steps, 1)
+    D, F, H, hd = w.d_model, w.ffn_dim, w.num_heads, w.head_dim
+    T = w.total_rows
+    flops = w.num_layers * (3.0 * T * (8 * D * D + 6 * D * F) + 14.0 * hd * H * batch.pairs)
+    flops_rep = w.num_layers * (3.0 * len(idx) * (8 * D * D + 6 * D * F) + 14.0 * hd * H * bbatch.pairs)
+    tf = flops / (g_ms * 1e-3) / 1e12
+    # mixed-precision roofline: Q/K/V projections and attention run bf16
+    # products, the O projection and the MLP fp32 products (reading of the
+    # harness precision); the shortest possible step runs each at its peak
+    bf16_flops = w.num_layers * (3.0 * T * 6 * D * D + 14.0 * hd * H * batch.pairs)
+    f32_flops = w.num_layers * 3.0 * T * (2 * D * D + 6 * D * F)
+    t_min = bf16_flops / (PEAK_BF16_TFLOPS * 1e12) + f32_flops / (PEAK_F32_TFLOPS * 1e12)
+    log(f"[bench] decoder: grouped {g_ms:.3f} ms/step ({g_lib:.3f} ms in this library's kernels), "
+        f"repeated-prefix {b_ms:.3f} ms ({b_lib:.3f} ms); speedup {b_ms / g_ms:.2f}x, flop ratio "
+        f"{flops_rep / flops:.2f}x; {tf:.1f} TFLOP/s")
+    return {"metric": "4-layer decoder fwd+bwd TFLOP/s on the packed layout; speedup vs repeated-prefix",
+            "value": round(tf, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": steps, "warmup": 2,
+            "ms_per_step": round(g_ms, 4), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1) hidden states, "
+            "N(0,0.02^2) weights, N(0,1) upstream gradient on response rows)",
+            "config": {"workload": w.name, "layers": w.num_layers, "d_model": D, "heads": H, "ffn": F,
+                       "rows": T, "repeated_prefix_rows": int(len(idx))},
+            "speedup_vs_repeated_prefix": round(b_ms / g_ms, 3),
+            "ideal_speedup_flops": round(flops_rep / flops, 3),
+            "library_kernel_ms_per_step": round(g_lib, 4),
+            "roofline": {"bound": "mfma", "kernel": "whole step (bf16 + fp32 products)",
+                         "achieved": round(tf, 1), "peak": round(flops / t_min / 1e12, 1),
+                         "unit": "TFLOP/s", "frac": round(t_min / (g_ms * 1e-3), 4), "traffic": None}}
+
+
 def grpo_head_bench(a, pg, torch) -> dict:
     """One step of the GRPO log-probability head on the head workload: pg_pack,
     pg_logprob_fwd, pg_grpo_loss, pg_logprob_bwd.  Credited 6 * N * V * d_model
@@ -402,6 +491,9 @@ def main(argv=None) -> int:
         return 0
     if a.grpo_head:
         print(json.dumps(grpo_head_bench(a, pg, torch)), flush=True)
+        return 0
+    if a.decoder:
+        print(json.dumps(decoder_bench(a, pg, torch)), flush=True)
         return 0
     groups = groups_of(w)
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
