@@ -361,10 +361,15 @@ def decoder_bench(a, pg, torch) -> dict:
         kt = pg.pg_kernel_times()
         pg.pg_kernel_timing(False)
         lib_ms = sum(t for n, (c, t) in kt.items()) / steps
+        timed.rope = kt["rope"]
         return s0.elapsed_time(s1) / steps, lib_ms, batch
 
     steps = max(2, a.steps // 4)
     g_ms, g_lib, batch = timed(groups, arrs["x"], arrs["dy"], steps, 2)
+    n_rope, t_rope = timed.rope
+    # RoPE: each launch reads and writes one bf16 [T, H, hd] tensor in place
+    rope_ms = t_rope / max(1, n_rope)
+    rope_gbs = 2 * w.total_rows * w.num_heads * w.head_dim * 2 / (rope_ms * 1e-3) / 1e9
     idx = []
     t = 0
     for g in w.groups:
@@ -401,6 +406,8 @@ def decoder_bench(a, pg, torch) -> dict:
             "speedup_vs_repeated_prefix": round(b_ms / g_ms, 3),
             "ideal_speedup_flops": round(flops_rep / flops, 3),
             "library_kernel_ms_per_step": round(g_lib, 4),
+            "rope": {"launches_per_step": n_rope // steps, "avg_ms": round(rope_ms, 4),
+                     "achieved_gbs": round(rope_gbs, 1), "peak_gbs": 8000.0},
             "roofline": {"bound": "mfma", "kernel": "whole step (bf16 + fp32 products)",
                          "achieved": round(tf, 1), "peak": round(flops / t_min / 1e12, 1),
                          "unit": "TFLOP/s", "frac": round(t_min / (g_ms * 1e-3), 4), "traffic": None}}

@@ -178,27 +178,30 @@ __global__ __launch_bounds__(kF32Threads) void dkdv_f32_kernel(
 }
 
 // Rotary embedding, rotate-half pairing; angle computed in double so that
-// large positions keep full precision.
+// large positions keep full precision.  One thread per (row, pair index):
+// the angle depends on those two only, so its cosine and sine are computed
+// once and applied to that pair of every head of the row.
 template <typename Tx>
 __global__ __launch_bounds__(256) void rope_kernel(Tx *__restrict__ x, const int32_t *__restrict__ pos,
                                                    int T, int H, int D, double log_theta,
                                                    int inverse) {
   const int half = D / 2;
-  const long long n = (long long)T * H * half;
   const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= n) return;
+  if (idx >= (long long)T * half) return;
   const int i = (int)(idx % half);
-  const long long th = idx / half;  // row * H + head
-  const int t = (int)(th / H);
+  const int t = (int)(idx / half);
   const double inv_freq = exp(-log_theta * (2.0 * i) / D);
   const double ang = (double)pos[t] * inv_freq;
   const float c = (float)cos(ang);
   float s = (float)sin(ang);
   if (inverse) s = -s;
-  Tx *row = x + th * D;
-  const float a = (float)row[i], b = (float)row[i + half];
-  row[i] = (Tx)(a * c - b * s);
-  row[i + half] = (Tx)(b * c + a * s);
+  Tx *row = x + (size_t)t * H * D;
+  for (int h = 0; h < H; ++h) {
+    Tx *r = row + (size_t)h * D;
+    const float a = (float)r[i], b = (float)r[i + half];
+    r[i] = (Tx)(a * c - b * s);
+    r[i + half] = (Tx)(b * c + a * s);
+  }
 }
 
 }  // namespace
@@ -257,8 +260,8 @@ hipError_t launch_bwd_dkdv_f32(const Plan &p, float scale, const void *q, const 
 
 hipError_t launch_rope(int T, int H, int D, pg_dtype t, void *x, const int32_t *pos, float theta,
                        int inverse, hipStream_t s) {
-  const long long n = (long long)T * H * (D / 2);
-  if (n == 0) return hipSuccess;
+  const long long n = (long long)T * (D / 2);  // one thread per (row, pair index)
+  if (n == 0 || H == 0) return hipSuccess;
   const dim3 grid((unsigned)((n + 255) / 256)), block(256);
   const double lt = log((double)theta);
   if (t == PG_BF16)
