@@ -132,3 +132,23 @@ def test_full_size_sampled():
     _say(f"[head] full: {len(ks)} rows logp {e_lp:.2e} lse {e_l:.2e}; dhidden {len(hs)} rows "
          f"{e_h:.2e}; dW {len(vs)} rows {e_w:.2e}")
     assert e_lp <= 2e-3 and e_l <= 2e-3 and e_h <= 1e-2 and e_w <= 1e-2
+
+
+def test_nothing_scored_gives_zero_gradients():
+    """No scored token (empty responses, and single-token responses of an
+    empty prefix): logp is empty, the loss is 0 and both gradients are
+    exactly zero (dweight from a product over zero rows)."""
+    groups = [(5, [0, 0]), (0, [1, 1, 0])]
+    w = HeadWorkload("none", tuple(Group(p, tuple(rs)) for p, rs in groups), 64, 300, seed=20)
+    arrs = draw_head_inputs(w)
+    adv = advantages_from_rewards(groups, arrs["rewards"])
+    # leave NaN in the allocator's cached blocks of the output sizes, so an
+    # output the library did not write would show
+    junk = [torch.full((300, 64), float("nan"), device="cuda"),
+            torch.full((w.total_rows, 64), float("nan"), device="cuda")]
+    del junk
+    batch, out = _run(w, arrs, adv)
+    assert batch.desc.num_scored == 0 and out["logp"].numel() == 0
+    assert float(out["loss"].cpu()[0]) == 0.0
+    assert torch.count_nonzero(out["dhidden"]).item() == 0
+    assert torch.count_nonzero(out["dW"]).item() == 0
