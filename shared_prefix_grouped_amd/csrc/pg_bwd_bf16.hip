@@ -244,8 +244,9 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
       *reinterpret_cast<bf16x8 *>(sQ + slot * C::BM * D + cdst[c]) = stq[c];
       *reinterpret_cast<bf16x8 *>(sdO + slot * C::BM * D + cdst[c]) = sto[c];
     }
-    // lanes 32..63 land in the unused half of the 64-float slot
-    if (wave < 2) (wave == 0 ? sL : sDl)[slot * 64 + lane] = stl;
+    // lanes 32..63 land in the unused half of the 64-float slot; the delta
+    // slot holds -delta, the start value of the dP accumulators
+    if (wave < 2) (wave == 0 ? sL : sDl)[slot * 64 + lane] = wave == 0 ? stl : -stl;
   };
   // Start of step n (slot k = n mod NSLOT): every wave has finished step
   // n-1 and slot k (written in step n-2) is visible.  Then (role A) slot k+2,
@@ -296,11 +297,16 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
         lds_cchar *cdO = slot_do(k);
         const float *cL = sL + k * 64;
         const float *cDl = sDl + k * 64;
+        // dp starts at -delta of its query row, so it ends as dP - delta
         f32x16 sc, dp;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          sc[r] = 0.f;
-          dp[r] = 0.f;
+        for (int rq = 0; rq < 4; ++rq) {
+          const f32x4 nD = *reinterpret_cast<const f32x4 *>(&cDl[rq * 8 + hi * 4]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            sc[rq * 4 + j] = 0.f;
+            dp[rq * 4 + j] = nD[j];
+          }
         }
 #pragma unroll
         for (int st = 0; st < D / 16; ++st) {
@@ -331,11 +337,7 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
         }
         // dS = P * (dP - delta)
 #pragma unroll
-        for (int rq = 0; rq < 4; ++rq) {
-          const f32x4 Dq = *reinterpret_cast<const f32x4 *>(&cDl[rq * 8 + hi * 4]);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) dp[rq * 4 + j] = p[rq * 4 + j] * (dp[rq * 4 + j] - Dq[j]);
-        }
+        for (int r = 0; r < 16; ++r) dp[r] = p[r] * dp[r];
         sX[kg][k & 1][0][lane] = pack8(p, 0);
         sX[kg][k & 1][1][lane] = pack8(p, 8);
         sX[kg][k & 1][2][lane] = pack8(dp, 0);
@@ -563,11 +565,12 @@ __global__ __launch_bounds__(256, 2) void dq_bf16_kernel(
 
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
+      // dp starts at -delta of the lane's query, so it ends as dP - delta
       f32x16 s, dp;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         s[r] = 0.f;
-        dp[r] = 0.f;
+        dp[r] = -Dq;
       }
 #pragma unroll
       for (int st = 0; st < D / 16; ++st) {
@@ -593,7 +596,7 @@ __global__ __launch_bounds__(256, 2) void dq_bf16_kernel(
         }
       }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] = s[r] * (dp[r] - Dq);
+      for (int r = 0; r < 16; ++r) s[r] = s[r] * dp[r];
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub) {
         const bf16x8 db = pack8(s, sub * 8);
