@@ -548,14 +548,18 @@ __global__ __launch_bounds__(256, 2) void dq_bf16_kernel(
     for (int r = 0; r < 16; ++r) dq[nb][r] = 0.f;
 
   if (nC > 0) issue(0);
+  // the fragment offsets carry the buffer of chunk ci (flipped every chunk),
+  // so the tile bases are constants and the reads take immediate offsets
+  static_assert(((C::BN * D * 2) & (C::BN * D * 2 - 1)) == 0, "buffer size a power of two");
+  lds_cchar *const cK = lds_bytes(sK);
+  lds_cchar *const cV = lds_bytes(sV);
   for (int ci = 0; ci < nC; ++ci) {
+    if (ci > 0) frag.flip(C::BN * D * 2);
     int c0, cend;
     chunk_range(ci, c0, cend);
     wait_async_loads();
     __syncthreads();
     if (ci + 1 < nC) issue(ci + 1);
-    lds_cchar *cK = lds_bytes(sK + (ci & 1) * C::BN * D);
-    lds_cchar *cV = lds_bytes(sV + (ci & 1) * C::BN * D);
     if (!wave_active) continue;
     const int clast = min(c0 + C::BN, cend) - 1;
     if (c0 > qwl) continue;

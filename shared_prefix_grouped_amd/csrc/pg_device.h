@@ -330,6 +330,18 @@ struct SwzFrags {
       tr_off[nb][1] = 2 * swz<D>(row + 8, col);
     }
   }
+  // Move every offset to the other half of a double buffer of `bytes` per
+  // half (a power of two above every offset's tile part): the buffer choice
+  // then lives in the offsets, and the tile base stays a constant.
+  __device__ __forceinline__ void flip(uint32_t bytes) {
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) row_off[st] ^= bytes;
+#pragma unroll
+    for (int nb = 0; nb < D / 32; ++nb) {
+      tr_off[nb][0] ^= bytes;
+      tr_off[nb][1] ^= bytes;
+    }
+  }
   // rows r0 + l32 (r0 a multiple of 16), 8 columns at 16 st + 8 hi
   __device__ __forceinline__ bf16x8 row(lds_cchar *tile, int r0, int st) const {
     return *reinterpret_cast<lds_bf16x8 *>(tile + row_off[st] + r0 * D * 2);
@@ -347,7 +359,16 @@ struct SwzFrags {
 // An LDS array as an address-space-3 byte pointer.
 __device__ __forceinline__ lds_cchar *lds_bytes(const void *p) { return (lds_cchar *)p; }
 
-__device__ __forceinline__ float wave_swap_halves(float x) { return __shfl_xor(x, 32); }
+// The values of x in lanes l mod 32 and l mod 32 + 32, in every lane l, in
+// that order: v_permlane32_swap exchanges the upper half of one register with
+// the lower half of another without going through the LDS.  Both halves then
+// combine the same two values in the same order.
+__device__ __forceinline__ void wave_halves(float x, float &lo, float &hi) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  lo = __uint_as_float(r[0]);
+  hi = __uint_as_float(r[1]);
+}
 
 // Pack 8 floats (registers r0..r0+7 of a 32x32 result) into bf16x8.
 __device__ __forceinline__ bf16x8 pack8(const f32x16 &s, int r0) {

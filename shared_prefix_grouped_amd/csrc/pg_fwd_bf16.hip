@@ -176,7 +176,11 @@ __global__ __launch_bounds__(256, FwdCfg<D>::OCC) void fwd_bf16_kernel(
     for (int b = 0; b < C::NB; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[b][r]);
-    mx = fmaxf(mx, wave_swap_halves(mx)) * scale_log2;
+    {
+      float lo, hi;
+      wave_halves(mx, lo, hi);
+      mx = fmaxf(lo, hi) * scale_log2;
+    }
     if (__builtin_amdgcn_ballot_w64(mx > m + kRescale)) {
       const float m_new = fmaxf(m, mx);
       const float alpha = fast_exp2(m - m_new);
@@ -212,7 +216,9 @@ __global__ __launch_bounds__(256, FwdCfg<D>::OCC) void fwd_bf16_kernel(
       }
   }
   if (!wave_active) return;
-  const float lt = l + wave_swap_halves(l);
+  float l_lo, l_hi;
+  wave_halves(l, l_lo, l_hi);
+  const float lt = l_lo + l_hi;
   if (!row_ok) return;
   const float inv = 1.f / lt;
   bf16 *op = O + ((size_t)qrow * Hq + h) * D;
