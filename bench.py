@@ -540,6 +540,25 @@ def main(argv=None) -> int:
                 "traffic": measured_traffic(w.name, dom),
                 "algorithmic_bytes_per_launch": alg, "avg_launch_ms": per_launch[dom]}
 
+    # every kernel of the step against its own roofline: algorithmic MFMA rate
+    # (attention kernels) and measured HBM bytes per launch from the committed
+    # counter profile (null once the kernel's sources differ from the profiled ones)
+    peak_mfma = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    kernel_roof = {}
+    for name, t_ms in per_launch.items():
+        if not t_ms:
+            continue
+        rec = {"avg_launch_ms": round(t_ms, 4)}
+        if name in KERNEL_FLOPS_PER_PAIR_D:
+            tf = KERNEL_FLOPS_PER_PAIR_D[name] * d * hq * pairs / (t_ms * 1e-3) / 1e12
+            rec.update({"algorithmic_tflops": round(tf, 1), "frac_mfma_peak": round(tf / peak_mfma, 4)})
+        hbm = measured_traffic(w.name, name)
+        if hbm is not None:
+            gbs = hbm / (t_ms * 1e-3) / 1e9
+            rec.update({"hbm_bytes": round(hbm), "hbm_gbs": round(gbs, 1),
+                        "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)})
+        kernel_roof[name] = rec
+
     if a.traffic_probe:
         n = (1 << 30) // 2
         src = torch.ones(n, dtype=torch.bfloat16, device="cuda")
@@ -596,6 +615,7 @@ def main(argv=None) -> int:
         "kernels_ms_per_launch": {n: round(v, 4) for n, v in per_launch.items() if v},
         "host_wall_ms_per_step": round(wall_ms, 4),
         "roofline": roof,
+        "kernel_rooflines": kernel_roof,
         "cpu_baseline": cpu,
         "context": "pages: prefix cost tends to 1/G of the baseline as P/R grows; 'up to 8x' for "
                    "long contexts (no hardware stated)",
