@@ -632,6 +632,94 @@ pg_status head_logits(rocblas_handle h, const void *hp, const void *weight, floa
                      "logits GEMM");
 }
 
+
+// ---------------------------------------------------------------- plan upload staging
+// pg_pack uploads the plan from pinned host buffers that the library owns, so
+// the call returns as soon as the copy is enqueued.  A buffer is reused once
+// the event recorded after its copy has completed; the buffers live until the
+// process ends.  When kMaxStaging uploads are still in flight, the call waits
+// for the oldest.
+struct Staging {
+  char *host = nullptr;
+  size_t cap = 0;
+  hipEvent_t done = nullptr;
+  bool busy = false;  // being filled by a caller (the event then says nothing)
+  uint64_t seq = 0;   // order of the last upload
+};
+
+struct StagingPool {
+  std::mutex mu;
+  std::vector<Staging> bufs;
+  uint64_t next_seq = 1;
+};
+
+StagingPool &staging_pool() {
+  static StagingPool p;
+  return p;
+}
+
+constexpr size_t kMaxStaging = 64;
+
+// A free pinned buffer of at least `bytes`, marked busy; its index in *idx.
+hipError_t take_staging(size_t bytes, size_t *idx) {
+  StagingPool &p = staging_pool();
+  std::lock_guard<std::mutex> lock(p.mu);
+  size_t best = SIZE_MAX, oldest = SIZE_MAX;
+  for (size_t i = 0; i < p.bufs.size(); ++i) {
+    Staging &b = p.bufs[i];
+    if (b.busy) continue;
+    if (oldest == SIZE_MAX || b.seq < p.bufs[oldest].seq) oldest = i;
+    if (b.cap >= bytes && hipEventQuery(b.done) == hipSuccess &&
+        (best == SIZE_MAX || b.cap < p.bufs[best].cap))
+      best = i;
+  }
+  if (best == SIZE_MAX && p.bufs.size() >= kMaxStaging && oldest != SIZE_MAX) {
+    // too many uploads in flight: wait for the oldest and reuse (or regrow) it
+    hipError_t e = hipEventSynchronize(p.bufs[oldest].done);
+    if (e != hipSuccess) return e;
+    best = oldest;
+  }
+  if (best != SIZE_MAX && p.bufs[best].cap < bytes) {
+    hipError_t e = hipHostFree(p.bufs[best].host);
+    p.bufs[best].host = nullptr;
+    p.bufs[best].cap = 0;
+    if (e != hipSuccess) return e;
+  }
+  if (best == SIZE_MAX) {
+    Staging b;
+    hipError_t e = hipEventCreateWithFlags(&b.done, hipEventDisableTiming);
+    if (e != hipSuccess) return e;
+    p.bufs.push_back(b);
+    best = p.bufs.size() - 1;
+  }
+  Staging &b = p.bufs[best];
+  if (b.cap < bytes) {
+    size_t cap = 4096;
+    while (cap < bytes) cap *= 2;
+    void *h = nullptr;
+    hipError_t e = hipHostMalloc(&h, cap, hipHostMallocDefault);
+    if (e != hipSuccess) return e;
+    b.host = static_cast<char *>(h);
+    b.cap = cap;
+  }
+  b.busy = true;
+  *idx = best;
+  return hipSuccess;
+}
+
+// After the copies from buffer idx were enqueued on s (or failed): record the
+// event that frees it and release it to the pool.
+hipError_t release_staging(size_t idx, hipStream_t s, bool enqueued) {
+  StagingPool &p = staging_pool();
+  std::lock_guard<std::mutex> lock(p.mu);
+  Staging &b = p.bufs[idx];
+  hipError_t e = enqueued ? hipEventRecord(b.done, s) : hipSuccess;
+  if (e != hipSuccess) e = hipStreamSynchronize(s);  // the event is unusable: drain instead
+  b.busy = false;
+  b.seq = p.next_seq++;
+  return e;
+}
+
 }  // namespace
 
 extern "C" {
@@ -670,16 +758,24 @@ pg_status pg_pack(const pg_groups *g, void *d_buf, size_t buf_bytes, int32_t *d_
   if (buf_bytes < L.total)
     return fail(PG_ERR_WORKSPACE, "descriptor buffer too small: need " + std::to_string(L.total) +
                                       " bytes, got " + std::to_string(buf_bytes));
-  std::vector<char> host(L.total);
-  pg_desc d;
-  serialize(g, hp, L, host.data(), nullptr, &d);
   const int64_t T = hp.T;
+  const size_t pos_off = align16(L.total);
+  const size_t need = pos_off + (d_pos_ids ? size_t(T) * 4 : 0);
+  size_t slot = 0;
+  hipError_t e = take_staging(need, &slot);
+  if (e != hipSuccess) return hip_status(e, "pg_pack staging buffer");
+  char *host = staging_pool().bufs[slot].host;  // the pool only appends: stable while busy
+  pg_desc d;
+  serialize(g, hp, L, host, nullptr, &d);
+  if (d_pos_ids && T > 0) std::memcpy(host + pos_off, hp.pos.data(), size_t(T) * 4);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = hipMemcpyAsync(d_buf, host.data(), L.total, hipMemcpyHostToDevice, s);
+  e = hipMemcpyAsync(d_buf, host, L.total, hipMemcpyHostToDevice, s);
   if (e == hipSuccess && d_pos_ids && T > 0)
-    e = hipMemcpyAsync(d_pos_ids, hp.pos.data(), size_t(T) * 4, hipMemcpyHostToDevice, s);
-  // the host staging vectors die with this call, so wait for the copies
-  if (e == hipSuccess) e = hipStreamSynchronize(s);
+    e = hipMemcpyAsync(d_pos_ids, host + pos_off, size_t(T) * 4, hipMemcpyHostToDevice, s);
+  // the buffer is reused only after the copies have run (or right away if
+  // nothing was enqueued)
+  const hipError_t r = release_staging(slot, s, e == hipSuccess);
+  if (e == hipSuccess) e = r;
   if (e != hipSuccess) return hip_status(e, "pg_pack copy");
   point_into(&d, L, static_cast<const char *>(d_buf));
   *out = d;
