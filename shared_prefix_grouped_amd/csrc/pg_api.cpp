@@ -838,18 +838,28 @@ pg_status pg_attn_bwd(const pg_desc *d, pg_dtype t, float softmax_scale, const v
   const size_t rows = align16(size_t(p.Hq) * size_t(p.T) * 4);
   float *lse2 = reinterpret_cast<float *>(static_cast<char *>(workspace) + rows);
   float *partial = reinterpret_cast<float *>(static_cast<char *>(workspace) + 2 * rows);
-  hipError_t e = timed(PG_KERNEL_BWD_PRE, s,
-                       [&] { return pg::launch_bwd_pre(p, t, o, dout, lse, delta, lse2, s); });
+  hipError_t e;
+  if (t == PG_BF16) {
+    // dQ first: it also writes delta and the base-2 logsumexp of its rows,
+    // which the dK/dV kernel reads
+    e = timed(PG_KERNEL_BWD_DQ, s, [&] {
+      return pg::launch_bwd_dq_bf16(p, scale, q, k, v, o, lse, lse2, delta, dout, dq, s);
+    });
+    if (e == hipSuccess)
+      e = timed(PG_KERNEL_BWD_DKDV, s, [&] {
+        return pg::launch_bwd_dkdv_bf16(p, scale, q, k, v, lse2, delta, dout, dk, dv, partial, s);
+      });
+    return hip_status(e, "pg_attn_bwd launch");
+  }
+  e = timed(PG_KERNEL_BWD_PRE, s,
+            [&] { return pg::launch_bwd_pre(p, t, o, dout, lse, delta, lse2, s); });
   if (e != hipSuccess) return hip_status(e, "pg_attn_bwd preprocess launch");
   e = timed(PG_KERNEL_BWD_DKDV, s, [&] {
-    return (t == PG_BF16) ? pg::launch_bwd_dkdv_bf16(p, scale, q, k, v, lse2, delta, dout, dk, dv,
-                                                     partial, s)
-                          : pg::launch_bwd_dkdv_f32(p, scale, q, k, v, lse2, delta, dout, dk, dv, s);
+    return pg::launch_bwd_dkdv_f32(p, scale, q, k, v, lse2, delta, dout, dk, dv, s);
   });
   if (e == hipSuccess)
     e = timed(PG_KERNEL_BWD_DQ, s, [&] {
-      return (t == PG_BF16) ? pg::launch_bwd_dq_bf16(p, scale, q, k, v, lse2, delta, dout, dq, s)
-                            : pg::launch_bwd_dq_f32(p, scale, q, k, v, lse2, delta, dout, dq, s);
+      return pg::launch_bwd_dq_f32(p, scale, q, k, v, lse2, delta, dout, dq, s);
     });
   return hip_status(e, "pg_attn_bwd launch");
 }

@@ -459,12 +459,17 @@ struct DqCfg {
   static constexpr int BN = 64;         // keys per chunk
 };
 
+// It also does the backward's preprocessing for the rows it owns (each row
+// and query head belongs to exactly one dq work item): delta = rowsum(dO * O)
+// and the base-2 logsumexp, used here and stored for the dK/dV kernel, which
+// runs after it.
 template <int D>
 __global__ __launch_bounds__(256, 2) void dq_bf16_kernel(
     const int32_t *__restrict__ q_tiles, const int32_t *__restrict__ row_lo,
     const bf16 *__restrict__ Q, const bf16 *__restrict__ K, const bf16 *__restrict__ V,
-    const float *__restrict__ LSE2, const float *__restrict__ Delta, const bf16 *__restrict__ dO,
-    bf16 *__restrict__ dQ, int T, int Hq, int Hkv, float scale_log2, float scale) {
+    const bf16 *__restrict__ O, const float *__restrict__ LSE, float *__restrict__ LSE2,
+    float *__restrict__ Delta, const bf16 *__restrict__ dO, bf16 *__restrict__ dQ, int T, int Hq,
+    int Hkv, float scale_log2, float scale) {
   using C = DqCfg<D>;
   // K and V chunks, double-buffered, row-major and swizzled: K is read as MFMA
   // rows for S^T = K Q^T and transposed for dQ^T += K^T dS^T; V as rows for
@@ -488,10 +493,10 @@ __global__ __launch_bounds__(256, 2) void dq_bf16_kernel(
   const int lo = row_ok ? row_lo[qrow] : 0;
   const int lo_first = wave_active ? row_lo[qw0] : 0;
   const int lo_last = wave_active ? row_lo[qwl] : 0;
-  const float negL = row_ok ? -LSE2[(size_t)h * T + qrow] : 0.f;
-  const float Dq = row_ok ? Delta[(size_t)h * T + qrow] : 0.f;
-
   bf16x8 qf[D / 16], of[D / 16];
+  // delta of the lane's row: this lane's half of the columns (16 st + 8 hi
+  // + j), then the other half from lane l ^ 32, added in that order in both
+  float dpart = 0.f;
   {
     const size_t base = ((size_t)qrow * Hq + h) * D + 8 * hi;
 #pragma unroll
@@ -499,6 +504,9 @@ __global__ __launch_bounds__(256, 2) void dq_bf16_kernel(
       if (row_ok) {
         qf[st] = *reinterpret_cast<const bf16x8 *>(Q + base + 16 * st);
         of[st] = *reinterpret_cast<const bf16x8 *>(dO + base + 16 * st);
+        const bf16x8 ov = *reinterpret_cast<const bf16x8 *>(O + base + 16 * st);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) dpart = fmaf((float)of[st][j], (float)ov[j], dpart);
       } else {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -506,6 +514,18 @@ __global__ __launch_bounds__(256, 2) void dq_bf16_kernel(
           of[st][j] = (__bf16)0.f;
         }
       }
+    }
+  }
+  float Dq, negL;
+  {
+    float d_lo, d_hi;
+    wave_halves(dpart, d_lo, d_hi);
+    Dq = d_lo + d_hi;
+    const float l2 = row_ok ? LSE[(size_t)h * T + qrow] * kLog2e : 0.f;
+    negL = -l2;
+    if (row_ok && hi == 0) {
+      Delta[(size_t)h * T + qrow] = Dq;
+      LSE2[(size_t)h * T + qrow] = l2;
     }
   }
 
@@ -680,19 +700,19 @@ hipError_t launch_bwd_dkdv_bf16(const Plan &p, float scale, const void *q, const
 }
 
 hipError_t launch_bwd_dq_bf16(const Plan &p, float scale, const void *q, const void *k,
-                              const void *v, const float *lse, const float *delta,
-                              const void *dout, void *dq, hipStream_t s) {
+                              const void *v, const void *o, const float *lse, float *lse2,
+                              float *delta, const void *dout, void *dq, hipStream_t s) {
   if (p.n_q_tiles == 0) return hipSuccess;
   const dim3 grid((unsigned)p.n_q_tiles * (unsigned)p.Hq), block(256);
   const float sl2 = scale * kLog2e;
   if (p.D == 128)
     hipLaunchKernelGGL(dq_bf16_kernel<128>, grid, block, 0, s, p.q_tiles, p.row_lo,
-                       (const bf16 *)q, (const bf16 *)k, (const bf16 *)v, lse, delta,
-                       (const bf16 *)dout, (bf16 *)dq, p.T, p.Hq, p.Hkv, sl2, scale);
+                       (const bf16 *)q, (const bf16 *)k, (const bf16 *)v, (const bf16 *)o, lse,
+                       lse2, delta, (const bf16 *)dout, (bf16 *)dq, p.T, p.Hq, p.Hkv, sl2, scale);
   else
     hipLaunchKernelGGL(dq_bf16_kernel<64>, grid, block, 0, s, p.q_tiles, p.row_lo,
-                       (const bf16 *)q, (const bf16 *)k, (const bf16 *)v, lse, delta,
-                       (const bf16 *)dout, (bf16 *)dq, p.T, p.Hq, p.Hkv, sl2, scale);
+                       (const bf16 *)q, (const bf16 *)k, (const bf16 *)v, (const bf16 *)o, lse,
+                       lse2, delta, (const bf16 *)dout, (bf16 *)dq, p.T, p.Hq, p.Hkv, sl2, scale);
   return hipGetLastError();
 }
 
