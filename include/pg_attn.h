@@ -106,7 +106,10 @@ typedef struct {
  *                Key row k is seen by exactly the query rows [k, row_hi[k]).
  *   q_tiles      [num_q_tiles][4] = {q0, q1, group start, prefix end}: query
  *                rows [q0, q1) of one group, q1 - q0 <= PG_TILE_Q, ordered by
- *                decreasing cost.
+ *                decreasing run time: the key chunks a forward / dQ work item
+ *                streams (64 rows each: the prefix keys up to q1, then the
+ *                keys from the response start of row q0), then the visible
+ *                (query, key) pairs.
  *   kv_tiles     [num_kv_tiles][4] = {k0, k1, q_end, prefix end}: key rows
  *                [k0, k1) of one group, k1 - k0 <= PG_TILE_KV, seen by query
  *                rows inside [k0, q_end), ordered by decreasing cost.

@@ -202,13 +202,23 @@ pg_status plan_batch(const pg_groups *g, HostPlan &hp) {
       hp.base_pairs += Lb * (Lb + 1) / 2;
       s += R;
     }
-    // query tiles: cost = number of visible keys summed over the tile's rows
+    // query tiles, ordered by run time: the K/V chunks the forward / dQ work
+    // item streams (prefix keys up to the tile's end, then the keys from its
+    // first row's response start), its waves running side by side; ties by
+    // the visible keys summed over the tile's rows.  (Ordered by visible keys
+    // alone, a short tile at a group's end -- few rows, but every prefix
+    // chunk -- would start last and run alone at the end of the launch.)
     for (int32_t q0 = g0; q0 < gend; q0 += PG_TILE_Q) {
       const int32_t q1 = std::min(gend, q0 + PG_TILE_Q);
-      int64_t cost = 0;
+      int64_t keys = 0;
       for (int32_t x = q0; x < q1; ++x)
-        cost += (x < pe) ? (x - g0 + 1) : (int64_t(P) + (x - row_lo[x] + 1));
-      qt.push_back({q0, q1, g0, pe, cost, int64_t(qt.size())});
+        keys += (x < pe) ? (x - g0 + 1) : (int64_t(P) + (x - row_lo[x] + 1));
+      const int64_t a_rows = std::min(pe, q1) - g0;
+      const int64_t b_rows = q1 - std::max(pe, row_lo[q0]);
+      const int64_t chunks = (a_rows > 0 ? ceil_div(a_rows, pg::kKvChunk) : 0) +
+                             (b_rows > 0 ? ceil_div(b_rows, pg::kKvChunk) : 0);
+      // chunks first: keys <= PG_TILE_Q * T < 2^37 and chunks < 2^25 (T < 2^30)
+      qt.push_back({q0, q1, g0, pe, (chunks << 37) + keys, int64_t(qt.size())});
     }
     // key tiles: cost = number of query rows seeing each key, summed
     for (int32_t k0 = g0; k0 < gend; k0 += PG_TILE_KV) {

@@ -456,7 +456,7 @@ struct DqCfg {
   static constexpr int BM = PG_TILE_Q;  // query rows per workgroup
   static constexpr int NW = BM / 32;
   static constexpr int NT = NW * 64;
-  static constexpr int BN = 64;         // keys per chunk
+  static constexpr int BN = kKvChunk;   // keys per chunk
 };
 
 // It also does the backward's preprocessing for the rows it owns (each row

@@ -30,7 +30,7 @@ struct FwdCfg {
   static constexpr int BM = PG_TILE_Q;  // query rows per workgroup
   static constexpr int NW = BM / 32;    // waves
   static constexpr int NT = NW * 64;    // threads
-  static constexpr int BN = 64;         // keys per chunk
+  static constexpr int BN = kKvChunk;   // keys per chunk
   static constexpr int NB = BN / 32;    // 32-key MFMA blocks per chunk
   static constexpr int OCC = 2;         // workgroups per CU (LDS: 4 * BN * D * 2 bytes each)
 };

@@ -26,6 +26,12 @@ struct Plan {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// Keys per K/V chunk of the bf16 forward and dQ kernels: a work item streams
+// its key segments through LDS in chunks of this many rows, one barrier step
+// each, so its run time follows its chunk count (the planner orders the query
+// tiles by it).
+constexpr int kKvChunk = 64;
+
 // Forward (writes o and lse for every row and query head).
 hipError_t launch_fwd_bf16(const Plan &p, float scale, const void *q, const void *k,
                            const void *v, void *o, float *lse, hipStream_t s);

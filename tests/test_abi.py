@@ -67,6 +67,30 @@ def _random_groups(rng, max_groups=4, max_p=300, max_r=200, max_g=6):
             for _ in range(int(rng.integers(1, max_groups + 1)))]
 
 
+def _tile_chunks(plan, q0, q1, g0, pe, chunk=64):
+    """64-key chunks a forward / dQ work item over rows [q0, q1) streams: the
+    prefix keys [g0, min(pe, q1)), then [max(pe, row_lo[q0]), q1)."""
+    a = min(pe, q1) - g0
+    b = q1 - max(pe, int(plan["row_lo"][q0]))
+    return (-(-a // chunk) if a > 0 else 0) + (-(-b // chunk) if b > 0 else 0)
+
+
+def test_query_tiles_ordered_by_streamed_chunks():
+    """At the headline shape the short last tile of the group (few rows, but
+    every prefix chunk) is among the first work items, not the last."""
+    from workloads import attention_workloads
+    w = attention_workloads()["bf16_gqa_g16_p8192"]
+    groups = [(g.prefix_len, list(g.resp_lens)) for g in w.groups]
+    plan = pg.pg_pack_host(groups, 32, 8, 128)
+    T = plan["total_rows"]
+    tiles = [tuple(int(x) for x in t) for t in plan["q_tiles"]]
+    last = [i for i, t in enumerate(tiles) if t[1] == T]
+    assert len(last) == 1 and tiles[last[0]][1] - tiles[last[0]][0] < pg.PG_TILE_Q
+    chunks = [_tile_chunks(plan, *t) for t in tiles]
+    assert chunks == sorted(chunks, reverse=True)
+    assert last[0] < len(tiles) // 2
+
+
 def test_planner_random_layouts():
     rng = np.random.default_rng(99)
     for _ in range(30):
@@ -78,7 +102,8 @@ def test_planner_random_layouts():
         assert (plan["pairs"], plan["baseline_pairs"]) == pair_counts(groups)
         vis = _visibility_from_plan(plan)
         assert int(vis.sum()) == plan["pairs"]
-        # query tiles partition the rows, stay in one group, cost-sorted
+        # query tiles partition the rows, stay in one group, and are ordered
+        # by the key chunks their work item streams, then by visible pairs
         covered = np.zeros(T, dtype=int)
         costs = []
         for q0, q1, g0, pe in plan["q_tiles"]:
@@ -87,7 +112,7 @@ def test_planner_random_layouts():
             gi = np.searchsorted(plan["group_start"], q0, side="right") - 1
             assert plan["group_start"][gi] == g0 and plan["prefix_end"][gi] == pe
             assert q1 <= plan["group_start"][gi + 1]
-            costs.append(int(vis[q0:q1].sum()))
+            costs.append((_tile_chunks(plan, q0, q1, g0, pe), int(vis[q0:q1].sum())))
         assert np.all(covered == 1)
         assert costs == sorted(costs, reverse=True)
         # key tiles partition the rows; q_end bounds every query that sees them
