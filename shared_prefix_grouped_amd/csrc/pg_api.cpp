@@ -270,6 +270,11 @@ pg_status plan_batch(const pg_groups *g, HostPlan &hp) {
     }
   }
   for (size_t i = 0; i < hp.items.size(); ++i) hp.items[i].order = int64_t(i);
+  // A dK/dV work item runs one barrier step per (query head, 32-row block) of
+  // its walk, so it is ordered by its block count first, then by its pairs
+  // (blocks < 2^25 and pairs <= PG_TILE_KV * T < 2^37 for T < 2^30).
+  for (KvItem &it : hp.items)
+    it.cost = (ceil_div(it.qb - it.qa, kQueryBlock) << 37) + it.cost;
 
   // longest-processing-time-first order; ties keep packed order
   auto by_cost = [](const auto &x, const auto &y) {

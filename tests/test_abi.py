@@ -136,7 +136,8 @@ def _check_kv_items(plan, vis, rep):
     Uncut key tiles appear whole; a cut tile's pieces split [k0, q_end) at
     32-row query blocks, number their float partial slots consecutively in
     query order, each hold at least 32 (query head, block) steps, and are
-    listed in kv_sums; the list is ordered by decreasing cost."""
+    listed in kv_sums; the list is ordered by decreasing walk length (32-row
+    blocks), then visible pairs."""
     items, sums = plan["kv_items"], plan["kv_sums"]
     tiles = {(int(k0), int(k1)): int(qend) for k0, k1, qend, _ in plan["kv_tiles"]}
     assert np.all(items[:, 5:] == 0)
@@ -145,9 +146,9 @@ def _check_kv_items(plan, vis, rep):
     for k0, k1, qa, qb, part, *_ in items.tolist():
         assert (k0, k1) in tiles and k0 <= qa < qb <= tiles[(k0, k1)]
         by_tile.setdefault((k0, k1), []).append((qa, qb, part))
-        costs.append(int(vis[qa:qb, k0:k1].sum()))
+        costs.append((-(-(qb - qa) // 32), int(vis[qa:qb, k0:k1].sum())))
     assert costs == sorted(costs, reverse=True)
-    assert sum(costs) == plan["pairs"]
+    assert sum(c[1] for c in costs) == plan["pairs"]
     assert set(by_tile) == set(tiles)
     cut = {(int(k0), int(k1)): (int(first), int(n)) for k0, k1, first, n in sums}
     used = []
