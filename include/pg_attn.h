@@ -183,10 +183,11 @@ size_t pg_pack_buffer_size(const pg_groups *g);
  * (>= pg_pack_buffer_size bytes, 16-byte aligned).  If `d_pos_ids` is not
  * NULL it receives int32 [T] position ids as in the repeated-prefix baseline:
  * prefix row t of a group -> t, row j of a response -> P + j (Pith review,
- * "What carries the argument").  The upload is enqueued on `stream` from a
- * pinned host buffer that the library owns (reused once the copy has run,
- * kept until the process ends), so the call does not wait for the GPU; the
- * caller's host arrays may be freed when it returns.  d_buf and d_pos_ids
+ * "What carries the argument").  The plan is written into a pinned,
+ * device-mapped host buffer that the library owns (reused once its copy has
+ * run, kept until the process ends) and copied into d_buf by a kernel enqueued
+ * on `stream`, so the call does not wait for the GPU; the caller's host arrays
+ * may be freed when it returns.  d_buf and d_pos_ids
  * hold the plan for work ordered after the call on `stream` (other streams
  * must wait for it).  Fills *out. */
 pg_status pg_pack(const pg_groups *g, void *d_buf, size_t buf_bytes, int32_t *d_pos_ids,

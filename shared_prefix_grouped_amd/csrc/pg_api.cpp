@@ -649,13 +649,17 @@ pg_status head_logits(rocblas_handle h, const void *hp, const void *weight, floa
 
 
 // ---------------------------------------------------------------- plan upload staging
-// pg_pack uploads the plan from pinned host buffers that the library owns, so
-// the call returns as soon as the copy is enqueued.  A buffer is reused once
-// the event recorded after its copy has completed; the buffers live until the
-// process ends.  When kMaxStaging uploads are still in flight, the call waits
-// for the oldest.
+// pg_pack writes the plan into a pinned, device-mapped host buffer that the
+// library owns, and a kernel on the caller's stream copies it into the
+// caller's device buffer, reading it over the bus: the call does not wait for
+// the GPU, and in stream order the upload is one more kernel, with no hand-off
+// to a copy engine.  The buffers are coherent (the GPU does not cache them),
+// reused once the event recorded after their copy has completed, and never
+// freed: they live until the process ends.  When kMaxStaging buffers exist and
+// none is free, the call waits for the oldest large enough one.
 struct Staging {
   char *host = nullptr;
+  void *dev = nullptr;  // its device address
   size_t cap = 0;
   hipEvent_t done = nullptr;
   bool busy = false;  // being filled by a caller (the event then says nothing)
@@ -682,42 +686,36 @@ hipError_t take_staging(size_t bytes, size_t *idx) {
   size_t best = SIZE_MAX, oldest = SIZE_MAX;
   for (size_t i = 0; i < p.bufs.size(); ++i) {
     Staging &b = p.bufs[i];
-    if (b.busy) continue;
+    if (b.busy || b.cap < bytes) continue;
     if (oldest == SIZE_MAX || b.seq < p.bufs[oldest].seq) oldest = i;
-    if (b.cap >= bytes && hipEventQuery(b.done) == hipSuccess &&
-        (best == SIZE_MAX || b.cap < p.bufs[best].cap))
+    if (hipEventQuery(b.done) == hipSuccess && (best == SIZE_MAX || b.cap < p.bufs[best].cap))
       best = i;
   }
   if (best == SIZE_MAX && p.bufs.size() >= kMaxStaging && oldest != SIZE_MAX) {
-    // too many uploads in flight: wait for the oldest and reuse (or regrow) it
+    // too many uploads in flight: wait for the oldest large enough buffer
     hipError_t e = hipEventSynchronize(p.bufs[oldest].done);
     if (e != hipSuccess) return e;
     best = oldest;
   }
-  if (best != SIZE_MAX && p.bufs[best].cap < bytes) {
-    hipError_t e = hipHostFree(p.bufs[best].host);
-    p.bufs[best].host = nullptr;
-    p.bufs[best].cap = 0;
-    if (e != hipSuccess) return e;
-  }
   if (best == SIZE_MAX) {
     Staging b;
-    hipError_t e = hipEventCreateWithFlags(&b.done, hipEventDisableTiming);
-    if (e != hipSuccess) return e;
-    p.bufs.push_back(b);
-    best = p.bufs.size() - 1;
-  }
-  Staging &b = p.bufs[best];
-  if (b.cap < bytes) {
     size_t cap = 4096;
     while (cap < bytes) cap *= 2;
     void *h = nullptr;
-    hipError_t e = hipHostMalloc(&h, cap, hipHostMallocDefault);
+    hipError_t e = hipHostMalloc(&h, cap, hipHostMallocMapped | hipHostMallocCoherent);
     if (e != hipSuccess) return e;
+    e = hipHostGetDevicePointer(&b.dev, h, 0);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&b.done, hipEventDisableTiming);
+    if (e != hipSuccess) {
+      (void)hipHostFree(h);  // never read by a kernel
+      return e;
+    }
     b.host = static_cast<char *>(h);
     b.cap = cap;
+    p.bufs.push_back(b);
+    best = p.bufs.size() - 1;
   }
-  b.busy = true;
+  p.bufs[best].busy = true;
   *idx = best;
   return hipSuccess;
 }
@@ -779,16 +777,25 @@ pg_status pg_pack(const pg_groups *g, void *d_buf, size_t buf_bytes, int32_t *d_
   size_t slot = 0;
   hipError_t e = take_staging(need, &slot);
   if (e != hipSuccess) return hip_status(e, "pg_pack staging buffer");
-  char *host = staging_pool().bufs[slot].host;  // the pool only appends: stable while busy
+  // the pool only appends, and a busy buffer is not touched by other calls
+  char *host;
+  char *dev;
+  {
+    StagingPool &pool = staging_pool();
+    std::lock_guard<std::mutex> lock(pool.mu);
+    host = pool.bufs[slot].host;
+    dev = static_cast<char *>(pool.bufs[slot].dev);
+  }
   pg_desc d;
   serialize(g, hp, L, host, nullptr, &d);
-  if (d_pos_ids && T > 0) std::memcpy(host + pos_off, hp.pos.data(), size_t(T) * 4);
+  const bool with_pos = d_pos_ids && T > 0;
+  if (with_pos) std::memcpy(host + pos_off, hp.pos.data(), size_t(T) * 4);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  e = hipMemcpyAsync(d_buf, host, L.total, hipMemcpyHostToDevice, s);
-  if (e == hipSuccess && d_pos_ids && T > 0)
-    e = hipMemcpyAsync(d_pos_ids, host + pos_off, size_t(T) * 4, hipMemcpyHostToDevice, s);
-  // the buffer is reused only after the copies have run (or right away if
-  // nothing was enqueued)
+  // L.total is a multiple of 16 (every array of the layout is 16-byte aligned)
+  e = pg::launch_upload(dev, d_buf, L.total, dev + pos_off, d_pos_ids,
+                        with_pos ? size_t(T) : 0, s);
+  // the buffer is reused only after the upload kernel has run (or right away
+  // if nothing was enqueued)
   const hipError_t r = release_staging(slot, s, e == hipSuccess);
   if (e == hipSuccess) e = r;
   if (e != hipSuccess) return hip_status(e, "pg_pack copy");

@@ -62,6 +62,12 @@ hipError_t launch_bwd_dq_f32(const Plan &p, float scale, const void *q, const vo
                              const void *v, const float *lse, const float *delta,
                              const void *dout, void *dq, hipStream_t s);
 
+// Plan upload: `bytes` (a multiple of 16) from src_dev to dst and npos int32
+// position ids from pos_src_dev to pos_dst, where the sources are device
+// addresses of pinned host memory; a kernel on stream s.
+hipError_t launch_upload(const void *src_dev, void *dst, size_t bytes, const void *pos_src_dev,
+                         int32_t *pos_dst, size_t npos, hipStream_t s);
+
 // Row gather (pack: the caller's prefix / response row buffers -> packed
 // rows) or scatter (unpack), row_bytes a multiple of 4.
 hipError_t launch_rows(const Plan &p, bool pack, void *packed, void *pre, void *resp,

@@ -86,6 +86,23 @@ hipError_t launch_rows_typed(const Plan &p, bool pack, void *packed, void *pre, 
   return hipGetLastError();
 }
 
+
+// Copy of the plan (n16 16-byte chunks) and of the position ids (npos int32)
+// from the caller's pinned host staging buffer, read over the bus through its
+// device address, into device memory: an ordinary kernel in stream order, so
+// the upload needs no hand-off to a copy engine between two kernels.
+__global__ __launch_bounds__(256) void upload_kernel(const uint4 *__restrict__ src,
+                                                     uint4 *__restrict__ dst, long long n16,
+                                                     const uint32_t *__restrict__ psrc,
+                                                     uint32_t *__restrict__ pdst,
+                                                     long long npos) {
+  const long long stride = (long long)gridDim.x * blockDim.x;
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride)
+    dst[i] = src[i];
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < npos; i += stride)
+    pdst[i] = psrc[i];
+}
+
 }  // namespace
 
 hipError_t launch_rows(const Plan &p, bool pack, void *packed, void *pre, void *resp,
@@ -93,6 +110,20 @@ hipError_t launch_rows(const Plan &p, bool pack, void *packed, void *pre, void *
   if (row_bytes % 16 == 0)
     return launch_rows_typed<uint4>(p, pack, packed, pre, resp, row_bytes, s);
   return launch_rows_typed<uint32_t>(p, pack, packed, pre, resp, row_bytes, s);
+}
+
+hipError_t launch_upload(const void *src_dev, void *dst, size_t bytes, const void *pos_src_dev,
+                         int32_t *pos_dst, size_t npos, hipStream_t s) {
+  const long long n16 = (long long)(bytes / 16);
+  const long long work = n16 > (long long)npos ? n16 : (long long)npos;
+  if (work == 0) return hipSuccess;
+  const long long want = (work + 255) / 256;
+  const unsigned blocks = (unsigned)(want < 1024 ? want : 1024);
+  hipLaunchKernelGGL(upload_kernel, dim3(blocks), dim3(256), 0, s,
+                     static_cast<const uint4 *>(src_dev), static_cast<uint4 *>(dst), n16,
+                     static_cast<const uint32_t *>(pos_src_dev),
+                     reinterpret_cast<uint32_t *>(pos_dst), (long long)npos);
+  return hipGetLastError();
 }
 
 }  // namespace pg
