@@ -174,7 +174,7 @@ def _kv_groups(hq: int, hkv: int, kv_heads: Optional[Iterable[int]]):
 
 
 def repeated_prefix_attention(groups, q, k, v, do=None, scale=None, kv_heads=None,
-                              check_prefix_copies=True) -> Dict[str, np.ndarray]:
+                              check_prefix_copies=True, members=None) -> Dict[str, np.ndarray]:
     """Baseline grouped attention: every [P; R_i] on its own, mapped back to packed rows.
 
     groups: (prefix_len, resp_lens) per group.  q, do: [T, Hq, d]; k, v: [T, Hkv, d].
@@ -187,6 +187,14 @@ def repeated_prefix_attention(groups, q, k, v, do=None, scale=None, kv_heads=Non
     causal attention.  Prefix rows take member 0's output and logsumexp (all
     members must agree, which is checked), and sum the gradient over the G
     copies; response rows take their own member's values.
+
+    members: optional subset of member sequences (indices in group-major
+    order, as member_sequences lists them).  Only those are evaluated: O and
+    LSE are filled on their rows (a group's prefix rows from its first listed
+    member; other rows stay zero) and the gradients are the sums over the
+    listed members only, so the sums over a partition of the members add up
+    to the full result (the prefix gradient is a sum over copies).  The
+    upstream gradient of a prefix row is still divided by the group's full G.
     """
     T, hq, d = q.shape
     hkv = k.shape[1]
@@ -194,18 +202,24 @@ def repeated_prefix_attention(groups, q, k, v, do=None, scale=None, kv_heads=Non
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     qh = [kv * rep + j for kv in kvs for j in range(rep)]
-    members, T2 = member_sequences(groups)
+    members_all, T2 = member_sequences(groups)
     if T2 != T:
         raise ValueError(f"packed rows {T} != sum of lengths {T2}")
     o = np.zeros((T, len(qh), d)); lse = np.zeros((len(qh), T))
     want_grad = do is not None
     if want_grad:
         dq = np.zeros((T, len(qh), d)); dk = np.zeros((T, len(kvs), d)); dv = np.zeros((T, len(kvs), d))
-    for m in members:
+    chosen = None if members is None else {int(i) for i in members}
+    first_seen = set()  # groups whose prefix output is already filled
+    for mi, m in enumerate(members_all):
+        if chosen is not None and mi not in chosen:
+            continue
         idx = m.rows
         if idx.size == 0:
             continue
         P = m.prefix_len
+        first = m.group not in first_seen
+        first_seen.add(m.group)
         for a, h in enumerate(qh):
             b = a // rep
             hk = kvs[b]
@@ -213,7 +227,7 @@ def repeated_prefix_attention(groups, q, k, v, do=None, scale=None, kv_heads=Non
             ks = k[idx, hk].astype(np.float64)
             vs = v[idx, hk].astype(np.float64)
             os_, ls_ = causal_attention_forward(qs, ks, vs, scale)
-            if m.member == 0:
+            if first:
                 o[idx[:P], a] = os_[:P]
                 lse[a, idx[:P]] = ls_[:P]
             elif check_prefix_copies and P:
@@ -302,6 +316,9 @@ def repeated_prefix_key_rows(groups, q, k, v, do, k_rows, kv_heads, scale=None) 
     after r in that sequence and over the query heads of the kv head, of the
     textbook softmax gradient.  Each contributing query needs its full
     softmax row, so the cost is a forward pass over the queries that follow r.
+    The softmax rows of a member sequence are computed once for all the
+    requested key rows it contains, from the earliest of them on: a query
+    before key r gives probability exactly 0 at r, so it adds exact zeros.
     Returns dk, dv [n_rows, n_kv_heads, d].
     """
     T, hq, d = q.shape
@@ -311,30 +328,38 @@ def repeated_prefix_key_rows(groups, q, k, v, do, k_rows, kv_heads, scale=None) 
     members, T2, owner = _row_member_map(groups)
     k_rows = [int(r) for r in k_rows]
     dk = np.zeros((len(k_rows), len(kv_heads), d)); dv = np.zeros_like(dk)
+    # member index -> [(output slot, position of the key row in the sequence)]
+    wanted: Dict[int, List[Tuple[int, int]]] = {}
     for ri, r in enumerate(k_rows):
         if r in owner:
-            seqs = [members[owner[r]]]
+            mis = [owner[r]]
         else:
-            seqs = [m for m in members if m.prefix[0] <= r < m.prefix[1]]
+            mis = [mi for mi, m in enumerate(members) if m.prefix[0] <= r < m.prefix[1]]
+        for mi in mis:
+            pos = int(np.nonzero(members[mi].rows == r)[0][0])
+            wanted.setdefault(mi, []).append((ri, pos))
+    for mi, slots in wanted.items():
+        m = members[mi]
+        idx = m.rows
+        L = idx.size
+        start = min(pos for _, pos in slots)
         for bi, hk in enumerate(kv_heads):
-            for m in seqs:
-                idx = m.rows
-                pos = int(np.nonzero(idx == r)[0][0])
-                L = idx.size
-                ks = k[idx, hk].astype(np.float64)
-                vs = v[idx, hk].astype(np.float64)
-                for j in range(rep):
-                    h = hk * rep + j
-                    qs = q[idx, h].astype(np.float64)
-                    dos = do[idx, h].astype(np.float64)
-                    dos[:m.prefix_len] /= m.group_size
-                    for r0 in range(pos, L, ROW_BLOCK):
-                        r1 = min(L, r0 + ROW_BLOCK)
-                        p, _ = _softmax_rows(_causal_scores(qs, ks, r0, r1, scale))
-                        dp = dos[r0:r1] @ vs[:r1].T
-                        ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
-                        dk[ri, bi] += scale * (ds[:, pos] @ qs[r0:r1])
-                        dv[ri, bi] += p[:, pos] @ dos[r0:r1]
+            ks = k[idx, hk].astype(np.float64)
+            vs = v[idx, hk].astype(np.float64)
+            for j in range(rep):
+                h = hk * rep + j
+                qs = q[idx, h].astype(np.float64)
+                dos = do[idx, h].astype(np.float64)
+                dos[:m.prefix_len] /= m.group_size
+                for r0 in range(start, L, ROW_BLOCK):
+                    r1 = min(L, r0 + ROW_BLOCK)
+                    p, _ = _softmax_rows(_causal_scores(qs, ks, r0, r1, scale))
+                    dp = dos[r0:r1] @ vs[:r1].T
+                    ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+                    for ri, pos in slots:
+                        if pos < r1:
+                            dk[ri, bi] += scale * (ds[:, pos] @ qs[r0:r1])
+                            dv[ri, bi] += p[:, pos] @ dos[r0:r1]
     return {"dk": dk, "dv": dv}
 
 

@@ -146,14 +146,18 @@ def repeated_prefix_decoder(groups, x, params, dy=None, num_heads=1, theta=10000
 
     groups: (prefix_len, resp_lens) per group; x: [T, D] packed; params as in
     decoder_member; dy: [T, D] or None.  members_only: optional list of member
-    indices (group-major) to evaluate, forward only (for sampled checks at
-    full size).  Returns {"y": [T, D] (rows of evaluated members), and with dy
-    "grads": summed parameter gradients and "x" [T, D]}.
+    indices (group-major) to evaluate (for checks at full size, where the
+    members can be spread over several calls).  Returns {"y": [T, D] (rows of
+    evaluated members, NaN elsewhere), and with dy "grads": parameter
+    gradients and "x" [T, D], summed over the evaluated members}.  Over a
+    partition of the members these partial sums add up to the full result;
+    the upstream gradient of a prefix row is divided by the group's full G
+    either way.
     """
     members, T = member_sequences(groups)
     x = np.asarray(x, np.float64)
     y = np.full((T, x.shape[1]), np.nan)
-    want = dy is not None and members_only is None
+    want = dy is not None
     total = None
     dx = np.zeros_like(x) if want else None
     for mi, m in enumerate(members):

@@ -373,3 +373,41 @@ def test_sampled_rows_forward_only_matches_full_oracle():
     assert np.allclose(fwd["o"], full["o"][rows][:, [0, 1]], atol=1e-12, rtol=0)
     assert np.allclose(fwd["lse"], full["lse"][[0, 1]][:, rows], atol=1e-12, rtol=0)
     assert not fwd["dq"].any()
+
+
+def test_key_rows_across_row_blocks_match_full_oracle(monkeypatch):
+    """Several key rows of one member sequence share its softmax rows, which
+    then start at the earliest of them and span several row blocks."""
+    import oracle.attention as oa
+    monkeypatch.setattr(oa, "ROW_BLOCK", 3)
+    groups = [(11, [6, 0, 9]), (4, [7])]
+    members, T = member_sequences(groups)
+    rng = np.random.default_rng(33)
+    q, k, v, do = _rand(T, 4, 2, 5, rng)
+    full = repeated_prefix_attention(groups, q, k, v, do)
+    rows = [0, 5, 10, 12, 16, 17, 25, 26, 30, 33]
+    kr = repeated_prefix_key_rows(groups, q, k, v, do, rows, [1, 0])
+    assert np.allclose(kr["dk"], full["dk"][rows][:, [1, 0]], atol=1e-13, rtol=0)
+    assert np.allclose(kr["dv"], full["dv"][rows][:, [1, 0]], atol=1e-13, rtol=0)
+
+
+def test_member_subsets_sum_to_full():
+    """members=: outputs on the listed members' rows equal the full oracle's,
+    and the gradients over a partition of the members add up to the full
+    gradients (the prefix gradient is a sum over copies, Lemma 2.1)."""
+    groups = [(8, [3, 5, 0, 4]), (0, [6]), (5, [2, 2])]
+    members, T = member_sequences(groups)
+    rng = np.random.default_rng(44)
+    q, k, v, do = _rand(T, 4, 2, 6, rng)
+    full = repeated_prefix_attention(groups, q, k, v, do)
+    parts = [[0, 2, 5], [1, 4], [3, 6]]
+    acc = {n: np.zeros_like(full[n]) for n in ("dq", "dk", "dv")}
+    for part in parts:
+        sub = repeated_prefix_attention(groups, q, k, v, do, members=part)
+        rows = np.concatenate([members[i].rows for i in part])
+        assert np.allclose(sub["o"][rows], full["o"][rows], atol=1e-13, rtol=0)
+        assert np.allclose(sub["lse"][:, rows], full["lse"][:, rows], atol=1e-13, rtol=0)
+        for n in acc:
+            acc[n] += sub[n]
+    for n in acc:
+        assert np.allclose(acc[n], full[n], atol=1e-13, rtol=0), n

@@ -165,3 +165,34 @@ def test_grouped_packed_rows_equal_baseline():
     y = _t_decoder(tx, tp, torch.from_numpy(position_ids(GROUPS)), grouped_attn)
     (y * torch.tensor(dy)).sum().backward()
     _compare(res, y, tp, tx)
+
+
+def test_member_subsets_sum_to_full():
+    """members_only with dy: the outputs of the listed members' rows equal the
+    full run's, and the gradients over a partition of the members add up to
+    the full gradients (prefix gradients are sums over the copies)."""
+    p, x, dy = _setup(5)
+    kw = dict(num_heads=H, theta=THETA, eps=EPS)
+    full = repeated_prefix_decoder(GROUPS, x, p, dy, **kw)
+    members, T = member_sequences(GROUPS)
+    acc_x = np.zeros_like(full["x"])
+    acc = None
+    for part in ([0, 3], [1, 2]):
+        sub = repeated_prefix_decoder(GROUPS, x, p, dy, members_only=part, **kw)
+        rows = np.concatenate([members[i].rows for i in part])
+        assert np.allclose(sub["y"][rows], full["y"][rows], atol=1e-12, rtol=0)
+        acc_x += sub["x"]
+        if acc is None:
+            acc = {n: ([a.copy() for a in v] if isinstance(v, list) else v.copy())
+                   for n, v in sub["grads"].items()}
+        else:
+            for n, v in sub["grads"].items():
+                if isinstance(v, list):
+                    for l in range(len(v)):
+                        acc[n][l] += v[l]
+                else:
+                    acc[n] += v
+    assert np.allclose(acc_x, full["x"], atol=1e-12, rtol=0)
+    for n, v in full["grads"].items():
+        for a, b in zip(acc[n] if isinstance(v, list) else [acc[n]], v if isinstance(v, list) else [v]):
+            assert np.allclose(a, b, atol=1e-12, rtol=0), n
