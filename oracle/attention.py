@@ -308,7 +308,8 @@ def repeated_prefix_rows(groups, q, k, v, do, q_rows, q_heads, scale=None) -> Di
     return {"o": o, "lse": lse, "dq": dq}
 
 
-def repeated_prefix_key_rows(groups, q, k, v, do, k_rows, kv_heads, scale=None) -> Dict[str, np.ndarray]:
+def repeated_prefix_key_rows(groups, q, k, v, do, k_rows, kv_heads, scale=None,
+                             members=None) -> Dict[str, np.ndarray]:
     """dK and dV of the baseline at sampled packed key rows.
 
     For key row r: sum over every member sequence containing r (all G for a
@@ -319,12 +320,16 @@ def repeated_prefix_key_rows(groups, q, k, v, do, k_rows, kv_heads, scale=None) 
     The softmax rows of a member sequence are computed once for all the
     requested key rows it contains, from the earliest of them on: a query
     before key r gives probability exactly 0 at r, so it adds exact zeros.
+    members: optional subset of member sequences (group-major indices); the
+    sums then run over those members only (partial sums, as in
+    repeated_prefix_attention).
     Returns dk, dv [n_rows, n_kv_heads, d].
     """
     T, hq, d = q.shape
     rep = hq // k.shape[1]
     if scale is None:
         scale = 1.0 / math.sqrt(d)
+    members_sel = None if members is None else {int(i) for i in members}
     members, T2, owner = _row_member_map(groups)
     k_rows = [int(r) for r in k_rows]
     dk = np.zeros((len(k_rows), len(kv_heads), d)); dv = np.zeros_like(dk)
@@ -336,6 +341,8 @@ def repeated_prefix_key_rows(groups, q, k, v, do, k_rows, kv_heads, scale=None) 
         else:
             mis = [mi for mi, m in enumerate(members) if m.prefix[0] <= r < m.prefix[1]]
         for mi in mis:
+            if members_sel is not None and mi not in members_sel:
+                continue
             pos = int(np.nonzero(members[mi].rows == r)[0][0])
             wanted.setdefault(mi, []).append((ri, pos))
     for mi, slots in wanted.items():

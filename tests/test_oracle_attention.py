@@ -389,6 +389,11 @@ def test_key_rows_across_row_blocks_match_full_oracle(monkeypatch):
     kr = repeated_prefix_key_rows(groups, q, k, v, do, rows, [1, 0])
     assert np.allclose(kr["dk"], full["dk"][rows][:, [1, 0]], atol=1e-13, rtol=0)
     assert np.allclose(kr["dv"], full["dv"][rows][:, [1, 0]], atol=1e-13, rtol=0)
+    # partial sums over a partition of the members add up to the same rows
+    parts = [repeated_prefix_key_rows(groups, q, k, v, do, rows, [1, 0], members=m)
+             for m in ([0, 3], [1], [2])]
+    assert np.allclose(sum(x["dk"] for x in parts), kr["dk"], atol=1e-13, rtol=0)
+    assert np.allclose(sum(x["dv"] for x in parts), kr["dv"], atol=1e-13, rtol=0)
 
 
 def test_member_subsets_sum_to_full():
