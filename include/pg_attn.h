@@ -252,6 +252,28 @@ pg_status pg_attn_bwd(const pg_desc *d, pg_dtype t, float softmax_scale, const v
                       const void *dout, void *dq, void *dk, void *dv, void *workspace,
                       size_t ws_bytes, void *stream);
 
+/* Bytes of device scratch the library keeps per GPU for pg_attn_bwd_noalloc. */
+#define PG_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* pg_attn_bwd without a workspace argument and without any allocation, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight training or serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments (minus the workspace), same kernels and bitwise the same results
+ * as pg_attn_bwd.  The scratch pg_attn_bwd_workspace_size reports lives in a
+ * device array of PG_NOALLOC_SCRATCH_BYTES that the library holds on every
+ * GPU it runs on until the process ends (its address is looked up on the
+ * first call on each device); a batch needing more returns PG_ERR_WORKSPACE
+ * before anything is enqueued.  The call enqueues only kernel launches: no
+ * hipMalloc, hipFree or allocating library routine, and no timing events
+ * (pg_kernel_timing does not cover it).  Every call on one GPU shares that
+ * GPU's array, which keeps the last call's contents; each call writes every
+ * scratch value it reads first, so nothing needs clearing.  Calls that
+ * overlap on one GPU (concurrent streams, or host threads without ordering)
+ * race on the array: order them on one stream. */
+pg_status pg_attn_bwd_noalloc(const pg_desc *d, pg_dtype t, float softmax_scale, const void *q,
+                              const void *k, const void *v, const void *o, const float *lse,
+                              const void *dout, void *dq, void *dk, void *dv, void *stream);
+
 /* Rotary position embedding at the baseline position ids, in place on x
  * [T, num_heads, head_dim] (PG_BF16 or PG_F32, rotate-half pairing: element i
  * with element i + d/2, angle pos * theta^(-2i/d)), computed in float32.

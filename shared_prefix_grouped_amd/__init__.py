@@ -35,7 +35,8 @@ PG_TILE_Q = 128
 PG_TILE_KV = 128
 
 EXPORTED = ("pg_pack_buffer_size", "pg_pack", "pg_pack_host", "pg_attn_fwd",
-            "pg_attn_bwd_workspace_size", "pg_attn_bwd", "pg_rope", "pg_pack_rows",
+            "pg_attn_bwd_workspace_size", "pg_attn_bwd", "pg_attn_bwd_noalloc", "pg_rope",
+            "pg_pack_rows",
             "pg_unpack_rows", "pg_logprob_workspace_size", "pg_logprob_fwd", "pg_grpo_loss",
             "pg_logprob_bwd", "pg_kernel_timing",
             "pg_kernel_times", "pg_kernel_name", "pg_last_error", "pg_version")
@@ -106,6 +107,8 @@ def lib() -> ctypes.CDLL:
     L.pg_attn_bwd_workspace_size.restype = sz
     L.pg_attn_bwd.argtypes = [Dp, ctypes.c_int, f32] + [vp] * 10 + [sz, vp]
     L.pg_attn_bwd.restype = ctypes.c_int
+    L.pg_attn_bwd_noalloc.argtypes = [Dp, ctypes.c_int, f32] + [vp] * 9 + [vp]
+    L.pg_attn_bwd_noalloc.restype = ctypes.c_int
     L.pg_rope.argtypes = [Dp, ctypes.c_int, vp, i32, i32, vp, f32, i32, vp]
     L.pg_rope.restype = ctypes.c_int
     L.pg_pack_rows.argtypes = [Dp, vp, vp, vp, sz, vp]
@@ -311,6 +314,28 @@ def pg_attn_bwd(batch: PackedBatch, q, k, v, o, lse, dout, softmax_scale: Option
     _check(L.pg_attn_bwd(ctypes.byref(d), code, _scale(softmax_scale), _vp(q), _vp(k), _vp(v),
                          _vp(o), _vp(lse), _vp(dout), _vp(dq), _vp(dk), _vp(dv), _vp(workspace),
                          workspace.numel() * workspace.element_size(), _stream_ptr(dev)))
+    return dq, dk, dv
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # PG_NOALLOC_SCRATCH_BYTES
+
+
+def pg_attn_bwd_noalloc(batch: PackedBatch, q, k, v, o, lse, dout, dq, dk, dv,
+                        softmax_scale: Optional[float] = None):
+    """pg_attn_bwd into caller-allocated dq, dk, dv with the library's own
+    fixed device scratch (no allocation inside the call)."""
+    torch = _torch()
+    d = batch.desc
+    T, hq, hkv, D = d.total_rows, d.num_q_heads, d.num_kv_heads, d.head_dim
+    dev = q.device
+    for name, x, shp in (("q", q, (T, hq, D)), ("k", k, (T, hkv, D)), ("v", v, (T, hkv, D)),
+                         ("o", o, (T, hq, D)), ("dout", dout, (T, hq, D)),
+                         ("dq", dq, (T, hq, D)), ("dk", dk, (T, hkv, D)), ("dv", dv, (T, hkv, D))):
+        _check_tensor(name, x, shp, q.dtype, dev)
+    _check_tensor("lse", lse, (hq, T), torch.float32, dev)
+    _check(lib().pg_attn_bwd_noalloc(ctypes.byref(d), _dtype_code(q.dtype), _scale(softmax_scale),
+                                     _vp(q), _vp(k), _vp(v), _vp(o), _vp(lse), _vp(dout), _vp(dq),
+                                     _vp(dk), _vp(dv), _stream_ptr(dev)))
     return dq, dk, dv
 
 

@@ -733,6 +733,101 @@ hipError_t release_staging(size_t idx, hipStream_t s, bool enqueued) {
   return e;
 }
 
+// ---------------------------------------------------------------- no-alloc backward scratch
+// pg_attn_bwd_noalloc keeps the backward's workspace (delta, the base-2
+// logsumexp and the partial dK/dV sums of cut key tiles) in this file-scope
+// device array instead of a caller buffer.  Each device that loads the
+// library holds its own copy until the process ends.  In host code the name
+// `scratch` is only a host-side stand-in for the symbol: its device address
+// is looked up once per device (with that device current) and kept here, and
+// only that address is ever handed to kernels.
+static __device__ __align__(256) unsigned char scratch[PG_NOALLOC_SCRATCH_BYTES];
+
+struct ScratchAddr {
+  std::mutex mu;
+  std::map<int, void *> ptr;  // device ordinal -> device address of `scratch`
+};
+ScratchAddr &scratch_addr() {
+  static ScratchAddr a;
+  return a;
+}
+
+// Device address of this device's scratch array (the current device).
+pg_status scratch_for_current_device(void **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  ScratchAddr &a = scratch_addr();
+  std::lock_guard<std::mutex> lock(a.mu);
+  auto it = a.ptr.find(dev);
+  if (it == a.ptr.end()) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    if (p == nullptr) return fail(PG_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    it = a.ptr.emplace(dev, p).first;
+  }
+  *out = it->second;
+  return PG_OK;
+}
+
+// The backward of pg_attn_bwd and pg_attn_bwd_noalloc (same kernels); with
+// `timing` false nothing but the launches is enqueued (no timing events).
+pg_status attn_bwd(const pg_desc *d, pg_dtype t, float softmax_scale, const void *q, const void *k,
+                   const void *v, const void *o, const float *lse, const void *dout, void *dq,
+                   void *dk, void *dv, void *workspace, hipStream_t s, bool timing) {
+  pg::Plan p = plan_of(d);
+  const float scale = resolve_scale(softmax_scale, p.D);
+  auto run = [&](int id, auto &&launch) -> hipError_t {
+    return timing ? timed(id, s, launch) : launch();
+  };
+  float *delta = static_cast<float *>(workspace);
+  const size_t rows = align16(size_t(p.Hq) * size_t(p.T) * 4);
+  float *lse2 = reinterpret_cast<float *>(static_cast<char *>(workspace) + rows);
+  float *partial = reinterpret_cast<float *>(static_cast<char *>(workspace) + 2 * rows);
+  hipError_t e;
+  if (t == PG_BF16) {
+    // dQ first: it also writes delta and the base-2 logsumexp of its rows,
+    // which the dK/dV kernel reads
+    e = run(PG_KERNEL_BWD_DQ, [&] {
+      return pg::launch_bwd_dq_bf16(p, scale, q, k, v, o, lse, lse2, delta, dout, dq, s);
+    });
+    if (e == hipSuccess)
+      e = run(PG_KERNEL_BWD_DKDV, [&] {
+        return pg::launch_bwd_dkdv_bf16(p, scale, q, k, v, lse2, delta, dout, dk, dv, partial, s);
+      });
+    return hip_status(e, "pg_attn_bwd launch");
+  }
+  e = run(PG_KERNEL_BWD_PRE, [&] { return pg::launch_bwd_pre(p, t, o, dout, lse, delta, lse2, s); });
+  if (e != hipSuccess) return hip_status(e, "pg_attn_bwd preprocess launch");
+  e = run(PG_KERNEL_BWD_DKDV, [&] {
+    return pg::launch_bwd_dkdv_f32(p, scale, q, k, v, lse2, delta, dout, dk, dv, s);
+  });
+  if (e == hipSuccess)
+    e = run(PG_KERNEL_BWD_DQ, [&] {
+      return pg::launch_bwd_dq_f32(p, scale, q, k, v, lse2, delta, dout, dq, s);
+    });
+  return hip_status(e, "pg_attn_bwd launch");
+}
+
+// Argument checks shared by both backward entry points.
+pg_status check_bwd(const pg_desc *d, pg_dtype t, const void *q, const void *k, const void *v,
+                    const void *o, const float *lse, const void *dout, const void *dq,
+                    const void *dk, const void *dv) {
+  pg_status st = check_desc(d);
+  if (st != PG_OK) return st;
+  if ((st = check_dtype(t)) != PG_OK) return st;
+  if (d->total_rows == 0) return PG_OK;
+  if ((st = check_ptrs({{q, "q"}, {k, "k"}, {v, "v"}, {o, "o"}, {lse, "lse"}, {dout, "dout"},
+                        {dq, "dq"}, {dk, "dk"}, {dv, "dv"}})) != PG_OK)
+    return st;
+  if (t == PG_BF16 && (size_t(d->total_rows) + 32) * size_t(d->num_q_heads) *
+                             size_t(d->head_dim) * 2 > size_t(UINT32_MAX))
+    return fail(PG_ERR_UNSUPPORTED,
+                "bf16 backward: q and dout must each be under 4 GiB (32-bit buffer offsets)");
+  return PG_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -838,52 +933,33 @@ pg_status pg_attn_bwd(const pg_desc *d, pg_dtype t, float softmax_scale, const v
                       const void *k, const void *v, const void *o, const float *lse,
                       const void *dout, void *dq, void *dk, void *dv, void *workspace,
                       size_t ws_bytes, void *stream) {
-  pg_status st = check_desc(d);
-  if (st != PG_OK) return st;
-  if ((st = check_dtype(t)) != PG_OK) return st;
-  if (d->total_rows == 0) return PG_OK;
-  if ((st = check_ptrs({{q, "q"}, {k, "k"}, {v, "v"}, {o, "o"}, {lse, "lse"}, {dout, "dout"},
-                        {dq, "dq"}, {dk, "dk"}, {dv, "dv"}, {workspace, "workspace"}})) != PG_OK)
-    return st;
-  if (t == PG_BF16 && (size_t(d->total_rows) + 32) * size_t(d->num_q_heads) *
-                             size_t(d->head_dim) * 2 > size_t(UINT32_MAX))
-    return fail(PG_ERR_UNSUPPORTED,
-                "bf16 backward: q and dout must each be under 4 GiB (32-bit buffer offsets)");
+  pg_status st = check_bwd(d, t, q, k, v, o, lse, dout, dq, dk, dv);
+  if (st != PG_OK || d->total_rows == 0) return st;
+  if ((st = check_ptrs({{workspace, "workspace"}})) != PG_OK) return st;
   const size_t need = pg_attn_bwd_workspace_size(d, t);
   if (ws_bytes < need)
     return fail(PG_ERR_WORKSPACE, "workspace too small: need " + std::to_string(need) +
                                       " bytes, got " + std::to_string(ws_bytes));
-  pg::Plan p = plan_of(d);
-  const float scale = resolve_scale(softmax_scale, p.D);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  float *delta = static_cast<float *>(workspace);
-  const size_t rows = align16(size_t(p.Hq) * size_t(p.T) * 4);
-  float *lse2 = reinterpret_cast<float *>(static_cast<char *>(workspace) + rows);
-  float *partial = reinterpret_cast<float *>(static_cast<char *>(workspace) + 2 * rows);
-  hipError_t e;
-  if (t == PG_BF16) {
-    // dQ first: it also writes delta and the base-2 logsumexp of its rows,
-    // which the dK/dV kernel reads
-    e = timed(PG_KERNEL_BWD_DQ, s, [&] {
-      return pg::launch_bwd_dq_bf16(p, scale, q, k, v, o, lse, lse2, delta, dout, dq, s);
-    });
-    if (e == hipSuccess)
-      e = timed(PG_KERNEL_BWD_DKDV, s, [&] {
-        return pg::launch_bwd_dkdv_bf16(p, scale, q, k, v, lse2, delta, dout, dk, dv, partial, s);
-      });
-    return hip_status(e, "pg_attn_bwd launch");
-  }
-  e = timed(PG_KERNEL_BWD_PRE, s,
-            [&] { return pg::launch_bwd_pre(p, t, o, dout, lse, delta, lse2, s); });
-  if (e != hipSuccess) return hip_status(e, "pg_attn_bwd preprocess launch");
-  e = timed(PG_KERNEL_BWD_DKDV, s, [&] {
-    return pg::launch_bwd_dkdv_f32(p, scale, q, k, v, lse2, delta, dout, dk, dv, s);
-  });
-  if (e == hipSuccess)
-    e = timed(PG_KERNEL_BWD_DQ, s, [&] {
-      return pg::launch_bwd_dq_f32(p, scale, q, k, v, lse2, delta, dout, dq, s);
-    });
-  return hip_status(e, "pg_attn_bwd launch");
+  return attn_bwd(d, t, softmax_scale, q, k, v, o, lse, dout, dq, dk, dv, workspace,
+                  static_cast<hipStream_t>(stream), true);
+}
+
+pg_status pg_attn_bwd_noalloc(const pg_desc *d, pg_dtype t, float softmax_scale, const void *q,
+                              const void *k, const void *v, const void *o, const float *lse,
+                              const void *dout, void *dq, void *dk, void *dv, void *stream) {
+  pg_status st = check_bwd(d, t, q, k, v, o, lse, dout, dq, dk, dv);
+  if (st != PG_OK || d->total_rows == 0) return st;
+  const size_t need = pg_attn_bwd_workspace_size(d, t);
+  if (need > size_t(PG_NOALLOC_SCRATCH_BYTES))
+    return fail(PG_ERR_WORKSPACE,
+                "pg_attn_bwd_noalloc: this batch needs " + std::to_string(need) +
+                    " bytes of scratch, more than the library's fixed " +
+                    std::to_string(size_t(PG_NOALLOC_SCRATCH_BYTES)) +
+                    "; use pg_attn_bwd with a caller workspace");
+  void *ws = nullptr;
+  if ((st = scratch_for_current_device(&ws)) != PG_OK) return st;
+  return attn_bwd(d, t, softmax_scale, q, k, v, o, lse, dout, dq, dk, dv, ws,
+                  static_cast<hipStream_t>(stream), false);
 }
 
 pg_status pg_rope(const pg_desc *d, pg_dtype t, void *x, int32_t num_heads, int32_t head_dim,
