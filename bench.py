@@ -184,40 +184,46 @@ class Runner:
 
 
 def cpu_baseline(w, arrs, budget_s, forward_only=False):
-    """The oracle as it stands, on kv head 0 and the first members of group 0."""
+    """The oracle as it stands, on kv head 0 and the first members of group 0,
+    with BLAS threads = this process's CPU affinity; plus the whole workload's
+    oracle time extrapolated from it (the oracle's cost per member sequence and
+    kv head grows with the member's causal pairs)."""
     from oracle.attention import pair_counts, repeated_prefix_attention
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()
-                       if i.get("user_api") == "blas"] or [1])
-    except Exception:  # pragma: no cover - threadpoolctl missing
-        threads = 1
+    from threadpoolctl import threadpool_limits
+    cores = len(os.sched_getaffinity(0))
     P, rs = w.groups[0].prefix_len, list(w.groups[0].resp_lens)
     rep = w.num_q_heads // w.num_kv_heads
     done, elapsed = [], 0.0
-    for i, r in enumerate(rs):
-        s = P + sum(rs[:i])
-        rows = np.concatenate([np.arange(P), np.arange(s, s + r)])
-        sub = {k: v[rows] for k, v in arrs.items()}
-        t0 = time.perf_counter()
-        repeated_prefix_attention([(P, [r])], sub["q"], sub["k"], sub["v"],
-                                  None if forward_only else sub["do"], kv_heads=[0])
-        elapsed += time.perf_counter() - t0
-        done.append(r)
-        log(f"[bench] cpu oracle: member {i} (P={P}, R={r}) done, {elapsed:.1f}s")
-        if elapsed >= budget_s:
-            break
-    pairs, _ = pair_counts([(P, done)])
+    with threadpool_limits(cores):
+        for i, r in enumerate(rs):
+            s = P + sum(rs[:i])
+            rows = np.concatenate([np.arange(P), np.arange(s, s + r)])
+            sub = {k: v[rows] for k, v in arrs.items()}
+            t0 = time.perf_counter()
+            repeated_prefix_attention([(P, [r])], sub["q"], sub["k"], sub["v"],
+                                      None if forward_only else sub["do"], kv_heads=[0])
+            elapsed += time.perf_counter() - t0
+            done.append(r)
+            log(f"[bench] cpu oracle: member {i} (P={P}, R={r}) done, {elapsed:.1f}s")
+            if elapsed >= budget_s:
+                break
+    pairs, sample_base = pair_counts([(P, done)])
+    _, full_base = pair_counts(groups_of(w))
     per_pair = 4.0 if forward_only else 14.0
     flops = per_pair * w.head_dim * rep * pairs
+    full_s = elapsed * (full_base * w.num_kv_heads) / sample_base
     return {
-        "value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+        "value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(cores),
         "kind": "oracle",
         "sample": (f"fp64 repeated-prefix oracle, kv head 0 ({rep} query heads), group 0 prefix "
                    f"P={P} with its first {len(done)} responses {done}{' (forward only)' if forward_only else ''}; "
                    f"{elapsed:.1f} s; credited {int(per_pair)}*d*heads*pairs of that grouped sub-batch "
                    f"({pairs} pairs)"),
         "seconds": elapsed,
+        "full_workload_seconds_extrapolated": round(full_s, 1),
+        "extrapolation": (f"extrapolated: sample seconds x (baseline causal pairs of every member x "
+                          f"{w.num_kv_heads} kv heads) / (baseline causal pairs of the sampled members x 1 "
+                          f"kv head) = {elapsed:.1f} x {full_base * w.num_kv_heads} / {sample_base}"),
     }
 
 

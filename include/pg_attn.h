@@ -31,9 +31,18 @@
  *   - Element type: PG_BF16 (bfloat16 storage, float32 accumulation) or
  *     PG_F32 (float32 throughout).  Outputs are in the input type, rounded to
  *     nearest even from float32.  head_dim 64 or 128.
- *   - Device pointers must be 16-byte aligned.  All device buffers are
- *     allocated and owned by the caller; the library never allocates device
- *     memory.
+ *   - Device pointers must be 16-byte aligned.  All tensors, descriptors and
+ *     workspaces are allocated and owned by the caller.
+ *   - State the library itself holds, per process, until it ends (nothing is
+ *     freed): (1) pg_pack's pinned, device-mapped host staging buffers, at
+ *     most 64, reused once the upload kernel that reads them has run; (2) one
+ *     rocBLAS handle per device, created by the first log-probability head
+ *     call on it; (3) pg_attn_bwd_noalloc's device scratch array,
+ *     PG_NOALLOC_SCRATCH_BYTES per device, placed by the HIP runtime when the
+ *     library's code objects are loaded on that device; (4) the kernel timing
+ *     table and its event pool (pg_kernel_timing); (5) the thread-local
+ *     message of pg_last_error.  None of it carries results from one call to
+ *     the next.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Kernels are
  *     enqueued on it; the call returns before they finish.
  *   - Results are bitwise reproducible for the same inputs, descriptor and
@@ -143,6 +152,8 @@ typedef struct {
  *   pred_start [T + 1], pred_list [num_scored]: for packed row t, the
  *                scored entries it predicts are pred_list[pred_start[t] ..
  *                pred_start[t + 1]), in increasing order.
+ *   max_walk_rows   the longest query-row range [qa, qb) of a kv_items
+ *                   entry (bounded by the largest group);
  *   pairs           unmasked (query, key) pairs per query head;
  *   baseline_pairs  the same count for the repeated-prefix layout (each
  *                   [P; R_i] on its own). */
@@ -153,6 +164,7 @@ typedef struct {
   int32_t num_kv_items, num_kv_sums, num_kv_parts;
   int32_t total_prefix_rows;
   int32_t num_scored;
+  int32_t max_walk_rows;
   int64_t pairs, baseline_pairs;
   const int32_t *row_lo;
   const int32_t *row_hi;
@@ -244,9 +256,12 @@ size_t pg_attn_bwd_workspace_size(const pg_desc *d, pg_dtype t);
  * given to pg_attn_fwd; outputs dq [T,Hq,d], dk, dv [T,Hkv,d] are fully
  * overwritten.  `workspace` is device scratch of at least
  * pg_attn_bwd_workspace_size bytes (contents need not be initialised).
- * PG_BF16 needs (T + 32) * Hq * d * 2 < 2^32 (q and dout under 4 GiB each:
- * the dK/dV kernel addresses them with 32-bit unsigned buffer offsets), else
- * PG_ERR_UNSUPPORTED. */
+ * PG_BF16 needs (max_walk_rows + 32) * Hq * d * 2 < 2^32 (the query rows one
+ * dK/dV work item walks, at most one group's, under 4 GiB of q: the kernel
+ * bases its buffer descriptors at the item's first query row and addresses
+ * the rest with 32-bit unsigned offsets) and Hq * T * 4 < 2^31 (the float
+ * [Hq, T] arrays it reads), else PG_ERR_UNSUPPORTED.  q and dout themselves
+ * may exceed 4 GiB. */
 pg_status pg_attn_bwd(const pg_desc *d, pg_dtype t, float softmax_scale, const void *q,
                       const void *k, const void *v, const void *o, const float *lse,
                       const void *dout, void *dq, void *dk, void *dv, void *workspace,

@@ -70,7 +70,7 @@ class PgDesc(ctypes.Structure):
                 ("num_q_tiles", ctypes.c_int32), ("num_kv_tiles", ctypes.c_int32),
                 ("num_kv_items", ctypes.c_int32), ("num_kv_sums", ctypes.c_int32),
                 ("num_kv_parts", ctypes.c_int32), ("total_prefix_rows", ctypes.c_int32),
-                ("num_scored", ctypes.c_int32),
+                ("num_scored", ctypes.c_int32), ("max_walk_rows", ctypes.c_int32),
                 ("pairs", ctypes.c_int64), ("baseline_pairs", ctypes.c_int64),
                 ("row_lo", _i32p), ("row_hi", _i32p), ("q_tiles", _i32p), ("kv_tiles", _i32p),
                 ("kv_items", _i32p), ("kv_sums", _i32p),
@@ -231,7 +231,7 @@ def pg_pack_host(groups: Sequence, num_q_heads: int, num_kv_heads: int, head_dim
         "row_lo": arr(d.row_lo, T), "row_hi": arr(d.row_hi, T),
         "q_tiles": arr(d.q_tiles, d.num_q_tiles, 4), "kv_tiles": arr(d.kv_tiles, d.num_kv_tiles, 4),
         "kv_items": arr(d.kv_items, d.num_kv_items, 8), "kv_sums": arr(d.kv_sums, d.num_kv_sums, 4),
-        "num_kv_parts": d.num_kv_parts,
+        "num_kv_parts": d.num_kv_parts, "max_walk_rows": d.max_walk_rows,
         "scored_row": arr(d.scored_row, d.num_scored), "scored_pred": arr(d.scored_pred, d.num_scored),
         "scored_resp": arr(d.scored_resp, d.num_scored), "pred_start": arr(d.pred_start, T + 1),
         "pred_list": arr(d.pred_list, d.num_scored),
@@ -306,11 +306,19 @@ def pg_attn_bwd(batch: PackedBatch, q, k, v, o, lse, dout, softmax_scale: Option
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
+    # the kernels write through raw pointers: caller-supplied outputs must be
+    # exactly the shape, type and layout they assume
+    for name, x, shp in (("dq", dq, (T, hq, D)), ("dk", dk, (T, hkv, D)), ("dv", dv, (T, hkv, D))):
+        _check_tensor(name, x, shp, q.dtype, dev)
     code = _dtype_code(q.dtype)
     L = lib()
     ws_bytes = L.pg_attn_bwd_workspace_size(ctypes.byref(d), code)
     if workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    elif (workspace.device != dev or not workspace.is_contiguous()
+          or workspace.numel() * workspace.element_size() < ws_bytes):
+        raise PgError(PG_ERR_WORKSPACE, f"workspace must be a contiguous buffer of at least "
+                                        f"{ws_bytes} bytes on {dev}")
     _check(L.pg_attn_bwd(ctypes.byref(d), code, _scale(softmax_scale), _vp(q), _vp(k), _vp(v),
                          _vp(o), _vp(lse), _vp(dout), _vp(dq), _vp(dk), _vp(dv), _vp(workspace),
                          workspace.numel() * workspace.element_size(), _stream_ptr(dev)))

@@ -138,7 +138,7 @@ constexpr int kQueryBlock = 32;
 // The complete plan in host memory, before it is laid out in one buffer.
 struct HostPlan {
   int64_t T = 0, n_resp = 0, pairs = 0, base_pairs = 0;
-  int32_t n_parts = 0;
+  int32_t n_parts = 0, max_walk = 0;
   std::vector<int32_t> row_lo, row_hi, pos, gstart, pend, pbefore, rstart, rlen, rgroup;
   // scored response rows (log-probability head): target row, predicting row,
   // response index; and per packed row the scored entries it predicts (CSR)
@@ -269,7 +269,10 @@ pg_status plan_batch(const pg_groups *g, HostPlan &hp) {
       hp.items.push_back({k0, k1, qa, qb, hp.n_parts++, cost, 0});
     }
   }
-  for (size_t i = 0; i < hp.items.size(); ++i) hp.items[i].order = int64_t(i);
+  for (size_t i = 0; i < hp.items.size(); ++i) {
+    hp.items[i].order = int64_t(i);
+    hp.max_walk = std::max(hp.max_walk, hp.items[i].qb - hp.items[i].qa);
+  }
   // A dK/dV work item runs one barrier step per (query head, 32-row block) of
   // its walk, so it is ordered by its block count first, then by its pairs
   // (blocks < 2^25 and pairs <= PG_TILE_KV * T < 2^37 for T < 2^30).
@@ -353,6 +356,7 @@ void serialize(const pg_groups *g, const HostPlan &hp, const Layout &L, char *bu
   d.num_kv_parts = hp.n_parts;
   d.total_prefix_rows = hp.pbefore[g->num_groups];
   d.num_scored = int32_t(hp.sc_row.size());
+  d.max_walk_rows = hp.max_walk;
   d.pairs = hp.pairs;
   d.baseline_pairs = hp.base_pairs;
   d.buf_bytes = L.total;
@@ -821,10 +825,17 @@ pg_status check_bwd(const pg_desc *d, pg_dtype t, const void *q, const void *k, 
   if ((st = check_ptrs({{q, "q"}, {k, "k"}, {v, "v"}, {o, "o"}, {lse, "lse"}, {dout, "dout"},
                         {dq, "dq"}, {dk, "dk"}, {dv, "dv"}})) != PG_OK)
     return st;
-  if (t == PG_BF16 && (size_t(d->total_rows) + 32) * size_t(d->num_q_heads) *
-                             size_t(d->head_dim) * 2 > size_t(UINT32_MAX))
-    return fail(PG_ERR_UNSUPPORTED,
-                "bf16 backward: q and dout must each be under 4 GiB (32-bit buffer offsets)");
+  if (t == PG_BF16) {
+    if (d->max_walk_rows < 0 || d->max_walk_rows > d->total_rows)
+      return fail(PG_ERR_INVALID_ARG, "descriptor is not one filled by pg_pack");
+    if ((size_t(d->max_walk_rows) + 32) * size_t(d->num_q_heads) * size_t(d->head_dim) * 2 >
+        size_t(UINT32_MAX))
+      return fail(PG_ERR_UNSUPPORTED,
+                  "bf16 backward: the query rows of one dK/dV work item (at most one group) "
+                  "must be under 4 GiB of q (32-bit buffer offsets from the item's first row)");
+    if (size_t(d->num_q_heads) * size_t(d->total_rows) * 4 >= (size_t(1) << 31))
+      return fail(PG_ERR_UNSUPPORTED, "bf16 backward: Hq * T * 4 must be under 2^31");
+  }
   return PG_OK;
 }
 

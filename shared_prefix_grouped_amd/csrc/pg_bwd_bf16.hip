@@ -202,13 +202,17 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
   constexpr int NA = C::NG * 64;            // role-A threads
   constexpr int CPT = C::BM * CPR / NA;     // chunks per A thread and tensor
   static_assert(CPT >= 1 && CPT * NA == C::BM * CPR, "chunks split evenly over role A");
-  // Buffer loads with one scalar descriptor per tensor: the row offset of
-  // the step is part of the vector offset, which the range check covers, so
-  // rows past the end of the batch read as zero (the visibility mask covers
-  // them); the head offset rides in the unchecked scalar offset and stays
-  // inside the row.
-  const __amdgpu_buffer_rsrc_t rQ = buffer_resource(Q, (size_t)T * q_row * sizeof(bf16));
-  const __amdgpu_buffer_rsrc_t rdO = buffer_resource(dO, (size_t)T * q_row * sizeof(bf16));
+  // Buffer loads with one scalar descriptor per tensor, based at the work
+  // item's first query row qa (the 64-bit base sits in the descriptor, so
+  // only the walk's own span, not the tensor, has to fit the 32-bit
+  // offsets): the row offset of the step from qa is part of the vector
+  // offset, which the range check covers, so rows past the end of the batch
+  // read as zero (the visibility mask covers them); the head offset rides in
+  // the unchecked scalar offset and stays inside the row.
+  const size_t q_avail = (size_t)(T - qa) * q_row * sizeof(bf16);
+  const uint32_t q_span = (uint32_t)min(q_avail, (size_t)0xFFFFFFFFu);
+  const __amdgpu_buffer_rsrc_t rQ = buffer_resource(Q + (size_t)qa * q_row, q_span);
+  const __amdgpu_buffer_rsrc_t rdO = buffer_resource(dO + (size_t)qa * q_row, q_span);
   const __amdgpu_buffer_rsrc_t rL = buffer_resource(wave == 0 ? LSE2 : Delta, (size_t)Hq * T * 4);
   int coff[CPT], cdst[CPT];  // chunk c of this thread: source byte offset, swizzled LDS element
 #pragma unroll
@@ -226,14 +230,16 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
     advance(stg);
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
-      // unsigned: the offset is a 32-bit unsigned byte count (tensors up to 4 GiB)
-      const int off = (int)((uint32_t)coff[c] + (uint32_t)c0 * (uint32_t)(q_row * sizeof(bf16)));
+      // unsigned 32-bit byte offset from row qa (walks up to 4 GiB of Q rows)
+      const int off = (int)((uint32_t)coff[c] +
+                            (uint32_t)(c0 - qa) * (uint32_t)(q_row * sizeof(bf16)));
       stq[c] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rQ, off, h * D * 2, 0));
       sto[c] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rdO, off, h * D * 2, 0));
     }
     if (wave < 2) {
       // every lane loads, so no lane mask is needed: lanes past the 32 rows,
       // and rows past the batch, use an offset past the resource (read as 0)
+      // (h T + row) * 4 < 2^31: the host checks Hq * T * 4 < 2^31
       const int off = (lane < C::BM && c0 + lane < T) ? (h * T + c0 + lane) * 4 : 0x7fffffff;
       stl = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rL, off, 0, 0));
     }

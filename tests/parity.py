@@ -7,6 +7,8 @@ Tolerances (fixed per element type):
   (prefix rows, response rows) so large prefix norms cannot hide response errors.
 """
 import math
+import os
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
@@ -89,3 +91,30 @@ def compare(gpu, ref, dtype_name, prefix_mask=None, grads=True, report=None):
     if report is not None:
         report.extend(msgs)
     return msgs
+
+
+def host_threads() -> int:
+    """CPU threads this process may use (its affinity mask), at most 16."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def pool_sum(fn, tasks, blas_threads=1):
+    """Sum of the dicts fn(task) returns (numpy arrays added, other values
+    taken from the first), computed in a thread pool: numpy releases the GIL
+    inside its ufuncs and BLAS calls, so independent oracle evaluations (one
+    member sequence, one kv head) run side by side."""
+    from threadpoolctl import threadpool_limits
+    tasks = list(tasks)
+    with threadpool_limits(blas_threads):
+        with ThreadPoolExecutor(max_workers=min(host_threads(), len(tasks))) as ex:
+            parts = list(ex.map(fn, tasks))
+    out = dict(parts[0])
+    for part in parts[1:]:
+        for key, val in part.items():
+            if isinstance(val, np.ndarray) and val.dtype.kind == "f":
+                out[key] = out[key] + val
+    return out

@@ -377,3 +377,52 @@ def test_python_binding_has_no_fallback():
     src = open(pg.__file__).read()
     assert "oracle" not in src.replace("no fallback", "")
     assert "import numpy" in src  # numpy only marshals host arrays for the planner
+
+
+def test_bf16_backward_bound_is_per_walk_not_per_tensor():
+    """The bf16 dK/dV kernel bases its Q/dO descriptors at each work item's
+    first query row, so the 32-bit limit applies to one walk (at most one
+    group), not to the whole tensor: the repeated-prefix layout of the
+    two-group workload (295,228 rows, 64 query heads: q is 4.8 GB) plans walks
+    of at most 33,280 rows, while one 300,000-row group is refused before
+    anything is launched."""
+    L = _lib()
+    rep_groups = tuple((32768, [512]) for _ in range(8)) + tuple(
+        (2048, [r]) for r in (1523, 1939, 1821, 1110, 1934, 2003, 1991, 283))
+    desc, _buf = _host_desc(rep_groups, 64, 8, 128)
+    assert desc.total_rows == 295228
+    assert desc.total_rows * 64 * 128 * 2 > 2 ** 32
+    items = np.frombuffer(ctypes.string_at(desc.kv_items, desc.num_kv_items * 32), dtype=np.int32)
+    items = items.reshape(-1, 8)
+    assert desc.max_walk_rows == int((items[:, 3] - items[:, 2]).max()) == 33280
+    assert (desc.max_walk_rows + 32) * 64 * 128 * 2 < 2 ** 32
+    big, _bbuf = _host_desc(((299000, [1000]),), 64, 8, 128)
+    p = ctypes.c_void_p(4096)
+    args = [p] * 10
+    ws = L.pg_attn_bwd_workspace_size(ctypes.byref(big), pg.PG_BF16)
+    st = L.pg_attn_bwd(ctypes.byref(big), pg.PG_BF16, ctypes.c_float(0.0), *args, ws, None)
+    assert st == pg.PG_ERR_UNSUPPORTED
+    assert "4 GiB" in L.pg_last_error().decode()
+
+
+def test_binding_checks_backward_outputs_before_launch():
+    """Caller-supplied dq / dk / dv / workspace of the wrong shape, type,
+    layout or size are refused by the binding before the library is called
+    (CPU tensors: a wrong one never reaches a kernel)."""
+    import torch
+    desc, _buf = _host_desc(((5, [3]),), 2, 1, 64)
+    batch = pg.PackedBatch(desc, None, None, ((5, (3,)),))
+    T, hq, hkv, d = 8, 2, 1, 64
+    q = torch.zeros((T, hq, d), dtype=torch.bfloat16)
+    kv = torch.zeros((T, hkv, d), dtype=torch.bfloat16)
+    lse = torch.zeros((hq, T), dtype=torch.float32)
+    bad = {"dq": torch.zeros((T, hq + 1, d), dtype=torch.bfloat16),
+           "dk": torch.zeros((T, hkv, d), dtype=torch.float32),
+           "dv": torch.zeros((T, hkv, 2 * d), dtype=torch.bfloat16)[:, :, ::2]}
+    for name, t in bad.items():
+        with pytest.raises(pg.PgError) as e:
+            pg.pg_attn_bwd(batch, q, kv, kv, q, lse, q, **{name: t})
+        assert name in str(e.value)
+    with pytest.raises(pg.PgError) as e:
+        pg.pg_attn_bwd(batch, q, kv, kv, q, lse, q, workspace=torch.zeros(4, dtype=torch.uint8))
+    assert e.value.status == pg.PG_ERR_WORKSPACE

@@ -1,10 +1,11 @@
 """GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
 
 Element by element on seeded inputs at sizes the oracle finishes in seconds
-(several tiles, ragged tails, varlen batches, GQA), on whole kv-head subsets of
-the full-size 32-head workload, and on sampled rows plus exact identities at
-the full sizes of the two largest workloads, launched exactly as the
-benchmark launches them.
+(several tiles, ragged tails, varlen batches, GQA), on whole kv heads of the
+full-size workloads (every row, every query head of the kv head), and on the
+longest prefix-key walks of the two-group workload, launched exactly as the
+benchmark launches them.  The oracle's member sequences run side by side in
+a thread pool at the full sizes.
 """
 import math
 import zlib
@@ -15,9 +16,9 @@ import time
 import numpy as np
 import pytest
 
-from oracle.attention import (repeated_prefix_attention, repeated_prefix_key_rows,
-                              repeated_prefix_rows)
-from tests.parity import compare, rel_fro, run_gpu, segment_rows, to_np
+from oracle.attention import (member_sequences, repeated_prefix_attention,
+                              repeated_prefix_key_rows, repeated_prefix_rows)
+from tests.parity import compare, host_threads, pool_sum, rel_fro, run_gpu, segment_rows, to_np
 from workloads import attention_workloads, draw_attention_inputs, scaled_down
 
 pytestmark = pytest.mark.gpu
@@ -111,16 +112,12 @@ def _sample_rows(groups, rng, extra=12):
 
 
 def _identities(groups, hq, hkv, arrs, out):
-    """Exact identities of softmax-attention gradients, per group and kv head.
-
-    sum_k dV[k] = sum over the group's rows and the kv head's query heads of dO;
-    sum_k dK[k] = 0;  <dQ, Q> = <dK, K>.  Returned as relative deviations.  The
-    inner-product sums cancel heavily (|sum| is ~1e-3 of sum |terms|), so their
-    deviation is scaled by sum |dQ * Q| + sum |dK * K|: an element-wise
-    relative error e in the gradients moves the difference by at most e times
-    that."""
+    """Exact identities of softmax-attention gradients, per group and kv head,
+    as relative deviations: sum_k dV[k] = the sum of dO over the group's rows
+    and the kv head's query heads, and sum_k dK[k] = 0.  (Neither sum cancels
+    much, so bf16 rounding of the stored gradients stays far below 1e-2.)"""
     rep = hq // hkv
-    dq, dk, dv = to_np(out["dq"]), to_np(out["dk"]), to_np(out["dv"])
+    dk, dv = to_np(out["dk"]), to_np(out["dv"])
     res = []
     t = 0
     for p, rs in groups:
@@ -132,82 +129,182 @@ def _identities(groups, hq, hkv, arrs, out):
             rhs = arrs["do"][sl, hs].astype(np.float64).sum(axis=(0, 1))
             e_v = np.linalg.norm(lhs - rhs) / np.linalg.norm(rhs)
             e_k = np.linalg.norm(dk[sl, hk].sum(axis=0)) / np.linalg.norm(dk[sl, hk])
-            tq = dq[sl, hs] * arrs["q"][sl, hs]
-            tk = dk[sl, hk] * arrs["k"][sl, hk]
-            e_qk = abs(float(tq.sum()) - float(tk.sum())) / float(np.abs(tq).sum() + np.abs(tk).sum())
-            res.append((e_v, e_k, e_qk))
+            res.append((e_v, e_k))
         t += n
     return np.array(res)
 
 
-def _sampled_check(w, q_heads, kv_heads, key_rows_fn):
+def _oracle_whole_kv_head(groups, arrs, hk):
+    """The full oracle restricted to kv head hk, its member sequences computed
+    side by side (each a partial sum; prefix O and LSE from member 0)."""
+    members, _ = member_sequences(groups)
+
+    def one(i):
+        r = repeated_prefix_attention(groups, arrs["q"], arrs["k"], arrs["v"], arrs["do"],
+                                      kv_heads=[hk], members=[i])
+        m = members[i]
+        if m.member != 0:  # the prefix outputs come from each group's member 0
+            r["o"][m.prefix[0]:m.prefix[1]] = 0.0
+            r["lse"][:, m.prefix[0]:m.prefix[1]] = 0.0
+        return r
+
+    return pool_sum(one, range(len(members)))
+
+
+def _gpu_kv_head(out, rows, hk, rep):
+    """GPU results on packed rows `rows` (a slice) for kv head hk and its query heads."""
+    qh = slice(hk * rep, (hk + 1) * rep)
+    return {"o": to_np(out["o"][rows, qh]), "lse": to_np(out["lse"][qh, rows]),
+            "dq": to_np(out["dq"][rows, qh]), "dk": to_np(out["dk"][rows, hk:hk + 1]),
+            "dv": to_np(out["dv"][rows, hk:hk + 1])}
+
+
+@pytest.fixture(scope="module")
+def headline_run():
+    """GQA 32/8, G = 16, P = 8192 workload on the GPU, as the benchmark runs it."""
+    w = attention_workloads()["bf16_gqa_g16_p8192"]
+    groups = _groups_of(w)
+    arrs = draw_attention_inputs(w)
+    _say(f"[parity] {w.name}: T={w.total_rows}, host threads {host_threads()}")
+    out = run_gpu(groups, w.num_q_heads, w.num_kv_heads, w.head_dim, arrs, torch.bfloat16)
+    return w, groups, arrs, out
+
+
+@pytest.mark.parametrize("hk", [0, 7])
+def test_bf16_gqa_g16_p8192_full_size_whole_kv_head(headline_run, hk):
+    """Every row (prefix and all 16 responses) of O, LSE, dQ, dK, dV for kv
+    head hk and its 4 query heads against the full oracle: every prefix key
+    row's whole walk (Lemma 2.1's sum over the 16 copies) is compared."""
+    w, groups, arrs, out = headline_run
+    rep = w.num_q_heads // w.num_kv_heads
+    t0 = time.time()
+    ref = _oracle_whole_kv_head(groups, arrs, hk)
+    gpu = _gpu_kv_head(out, slice(0, w.total_rows), hk, rep)
+    msgs = compare(gpu, ref, "bf16", prefix_mask=segment_rows(groups))
+    _say(f"[parity] {w.name} kv head {hk}: oracle {time.time() - t0:.1f}s; " + "; ".join(msgs))
+
+
+def test_bf16_gqa_g16_p8192_full_size_identities(headline_run):
+    w, groups, arrs, out = headline_run
+    ids = _identities(groups, w.num_q_heads, w.num_kv_heads, arrs, out)
+    _say(f"[parity] {w.name}: identity max deviations dV-sum {ids[:, 0].max():.2e}, "
+         f"dK-sum {ids[:, 1].max():.2e}")
+    assert ids[:, 0].max() <= 1e-2 and ids[:, 1].max() <= 2e-2
+
+
+@pytest.fixture(scope="module")
+def varlen_run():
+    """Two-group GQA 64/8 workload (P = 32768 x 8 responses of 512, then
+    P = 2048 x 8 ragged responses) on the GPU, as the benchmark runs it."""
+    w = attention_workloads()["bf16_varlen_2groups"]
     groups = _groups_of(w)
     t0 = time.time()
     arrs = draw_attention_inputs(w)
     _say(f"[parity] {w.name}: inputs drawn in {time.time() - t0:.1f}s, T={w.total_rows}")
     out = run_gpu(groups, w.num_q_heads, w.num_kv_heads, w.head_dim, arrs, torch.bfloat16)
-    rng = np.random.default_rng(w.seed + 100)
-    rows = _sample_rows(groups, rng)
+    return w, groups, arrs, out
+
+
+def _group_slice(groups, gi):
+    t = 0
+    for j, (p, rs) in enumerate(groups):
+        n = p + sum(rs)
+        if j == gi:
+            return slice(t, t + n)
+        t += n
+    raise IndexError(gi)
+
+
+def test_bf16_varlen_2groups_group1_whole_kv_head(varlen_run):
+    """Group 1 (P = 2048, responses 128..2048) in full for kv head 5 and its 8
+    query heads.  Groups are independent, so the oracle runs on group 1's rows
+    alone."""
+    w, groups, arrs, out = varlen_run
+    rep = w.num_q_heads // w.num_kv_heads
+    sl = _group_slice(groups, 1)
+    sub = {n: a[sl] for n, a in arrs.items()}
     t0 = time.time()
-    ref = repeated_prefix_rows(groups, arrs["q"], arrs["k"], arrs["v"], arrs["do"], rows, q_heads)
-    o = to_np(out["o"][rows][:, q_heads])
-    lse = to_np(out["lse"][q_heads][:, rows])
-    dq = to_np(out["dq"][rows][:, q_heads])
+    ref = _oracle_whole_kv_head([groups[1]], sub, 5)
+    gpu = _gpu_kv_head(out, sl, 5, rep)
+    msgs = compare(gpu, ref, "bf16", prefix_mask=segment_rows([groups[1]]))
+    _say(f"[parity] {w.name} group 1 kv head 5: oracle {time.time() - t0:.1f}s; " + "; ".join(msgs))
+
+
+def test_bf16_varlen_2groups_group0_prefix_key_rows(varlen_run):
+    """dK/dV of group 0's prefix key rows at key-tile boundaries near the
+    prefix end and in the middle of the prefix, for kv heads 0 and 7 (8 query
+    heads each): each is the sum over the 8 copies of the 32768-row prefix,
+    walked over every later prefix row and all 8 responses.  Plus the first
+    and last rows of each response as keys."""
+    w, groups, arrs, out = varlen_run
+    sl = _group_slice(groups, 0)
+    p0, r0 = groups[0]
+    sub = {n: a[sl] for n, a in arrs.items()}
+    krows = [30719, 30720, 32511, 32512, 32639, 32640, 32767]
+    s = p0
+    for r in r0:
+        krows += [s, s + r - 1]
+        s += r
+    kv = [0, 7]
+    n_mem = len(r0)
+    t0 = time.time()
+    parts = {}
+
+    def one(t):
+        return t, repeated_prefix_key_rows([groups[0]], sub["q"], sub["k"], sub["v"], sub["do"],
+                                           krows, [t[0]], members=[t[1]])
+
+    from concurrent.futures import ThreadPoolExecutor
+    from threadpoolctl import threadpool_limits
+    tasks = [(hk, i) for hk in kv for i in range(n_mem)]
+    with threadpool_limits(1), ThreadPoolExecutor(max_workers=host_threads()) as ex:
+        for (hk, i), r in ex.map(one, tasks):
+            acc = parts.setdefault(hk, {"dk": 0.0, "dv": 0.0})
+            acc["dk"] = acc["dk"] + r["dk"][:, 0]
+            acc["dv"] = acc["dv"] + r["dv"][:, 0]
+    g0 = sl.start
+    for hk in kv:
+        dk = to_np(out["dk"][[g0 + r for r in krows], hk])
+        dv = to_np(out["dv"][[g0 + r for r in krows], hk])
+        npre = sum(r < p0 for r in krows)
+        e = {"dk prefix": rel_fro(dk[:npre], parts[hk]["dk"][:npre]),
+             "dv prefix": rel_fro(dv[:npre], parts[hk]["dv"][:npre]),
+             "dk response": rel_fro(dk[npre:], parts[hk]["dk"][npre:]),
+             "dv response": rel_fro(dv[npre:], parts[hk]["dv"][npre:])}
+        _say(f"[parity] {w.name} group 0 kv head {hk}, {len(krows)} key rows: oracle "
+             f"{time.time() - t0:.1f}s; " + "; ".join(f"{k} rel-fro {v:.3e}" for k, v in e.items()))
+        assert all(v <= 1e-2 for v in e.values()), e
+
+
+def test_bf16_varlen_2groups_group0_sampled_query_rows(varlen_run):
+    """O, LSE and dQ of sampled group-0 query rows (prefix start and end, tile
+    boundaries, every response's first and last row, random rows) for query
+    heads 0 and 63."""
+    w, groups, arrs, out = varlen_run
+    sl = _group_slice(groups, 0)
+    sub = {n: a[sl] for n, a in arrs.items()}
+    rng = np.random.default_rng(w.seed + 100)
+    rows = _sample_rows([groups[0]], rng)
+    heads = [0, 63]
+    t0 = time.time()
+    ref = repeated_prefix_rows([groups[0]], sub["q"], sub["k"], sub["v"], sub["do"], rows, heads)
+    o = to_np(out["o"][rows][:, heads])
+    lse = to_np(out["lse"][heads][:, rows])
+    dq = to_np(out["dq"][rows][:, heads])
     e_o = float(np.max(np.abs(o - ref["o"])))
     e_l = float(np.max(np.abs(lse - ref["lse"])))
     e_q = rel_fro(dq, ref["dq"])
-    _say(f"[parity] {w.name}: {len(rows)} rows x {len(q_heads)} heads, oracle "
+    _say(f"[parity] {w.name} group 0: {len(rows)} rows x {len(heads)} heads, oracle "
          f"{time.time() - t0:.1f}s: o max-abs {e_o:.3e}, lse max-abs {e_l:.3e}, dq rel-fro {e_q:.3e}")
     assert e_o <= 2e-2 and e_l <= 1e-3 and e_q <= 1e-2
-    krows = key_rows_fn(groups)
-    t0 = time.time()
-    kref = repeated_prefix_key_rows(groups, arrs["q"], arrs["k"], arrs["v"], arrs["do"], krows,
-                                    kv_heads)
-    dk = to_np(out["dk"][krows][:, kv_heads])
-    dv = to_np(out["dv"][krows][:, kv_heads])
-    e_k, e_v = rel_fro(dk, kref["dk"]), rel_fro(dv, kref["dv"])
-    _say(f"[parity] {w.name}: {len(krows)} key rows, oracle {time.time() - t0:.1f}s: "
-         f"dk rel-fro {e_k:.3e}, dv rel-fro {e_v:.3e}")
-    assert e_k <= 1e-2 and e_v <= 1e-2
+
+
+def test_bf16_varlen_2groups_full_size_identities(varlen_run):
+    w, groups, arrs, out = varlen_run
     ids = _identities(groups, w.num_q_heads, w.num_kv_heads, arrs, out)
     _say(f"[parity] {w.name}: identity max deviations dV-sum {ids[:, 0].max():.2e}, "
-         f"dK-sum {ids[:, 1].max():.2e}, <dQ,Q>-<dK,K> {ids[:, 2].max():.2e}")
-    assert ids[:, 0].max() <= 1e-2 and ids[:, 1].max() <= 2e-2 and ids[:, 2].max() <= 1e-2
-    return out
-
-
-def _resp_key_rows(groups, per_group=4):
-    rows = []
-    t = 0
-    for p, rs in groups:
-        s = t + p
-        for i, r in enumerate(rs):
-            if r and i < per_group:
-                rows += [s, s + r - 1]
-            s += r
-        t = s
-    return rows
-
-
-def test_bf16_gqa_g16_p8192_full_size_sampled():
-    w = attention_workloads()["bf16_gqa_g16_p8192"]
-
-    def keys(groups):
-        p = groups[0][0]
-        return [p - 1] + _resp_key_rows(groups, 3)
-
-    _sampled_check(w, q_heads=[0, 13, 31], kv_heads=[0, 7], key_rows_fn=keys)
-
-
-def test_bf16_varlen_2groups_full_size_sampled():
-    w = attention_workloads()["bf16_varlen_2groups"]
-
-    def keys(groups):
-        (p0, r0), (p1, r1) = groups
-        g1 = p0 + sum(r0)
-        return [g1 + p1 - 1] + _resp_key_rows(groups, 2)
-
-    _sampled_check(w, q_heads=[0, 63], kv_heads=[3], key_rows_fn=keys)
+         f"dK-sum {ids[:, 1].max():.2e}")
+    assert ids[:, 0].max() <= 1e-2 and ids[:, 1].max() <= 2e-2
 
 
 @pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("f32", 128), ("f32", 64)])
@@ -283,18 +380,20 @@ def test_empty_batch():
     assert o.shape == (0, 2, 64) and dq.shape == (0, 2, 64)
 
 
-def test_bf16_tensors_over_2gib():
-    """Q and dO of 2.3 GB each (17 copies of a 16384-row prefix + 256-row
-    response, GQA 32/8): the dK/dV kernel's 32-bit buffer offsets pass 2^31.
-    The last group, whose rows all lie past 2 GiB, is checked against the
-    oracle on sampled query rows and on key rows near the prefix end and in
-    the response (each seen by at most 257 query rows)."""
+def test_bf16_tensors_over_4gib():
+    """Q and dO of 4.5 GB each (33 copies of a 16384-row prefix + 256-row
+    response, GQA 32/8): the dK/dV kernel bases its buffer descriptors at
+    each work item's first query row, so walks past 2^31 and 2^32 bytes of Q
+    use the same 32-bit offsets.  The last group, whose rows all lie past
+    4 GiB, is checked against the oracle on sampled query rows and on key
+    rows near the prefix end and in the response (each seen by at most 257
+    query rows)."""
     import shared_prefix_grouped_amd as pg
-    P, R, G, hq, hkv, d = 16384, 256, 17, 32, 8, 128
+    P, R, G, hq, hkv, d = 16384, 256, 33, 32, 8, 128
     groups = [(P, [R])] * G
     T = G * (P + R)
-    assert (T - (P + R)) * hq * d * 2 > 2 ** 31  # the last group starts past 2 GiB
-    _say(f"[parity] over-2GiB: T={T}, q bytes {T * hq * d * 2 / 2**30:.2f} GiB")
+    assert (T - (P + R)) * hq * d * 2 > 2 ** 32  # the last group starts past 4 GiB
+    _say(f"[parity] over-4GiB: T={T}, q bytes {T * hq * d * 2 / 2**30:.2f} GiB")
     gen = torch.Generator(device="cuda").manual_seed(21)
     q, k, v, do = (torch.randn((T, h, d), generator=gen, device="cuda").to(torch.bfloat16)
                    for h in (hq, hkv, hkv, hq))
@@ -312,12 +411,12 @@ def test_bf16_tensors_over_2gib():
     e_o = float(np.max(np.abs(to_np(o[gr][:, heads]) - ref["o"])))
     e_l = float(np.max(np.abs(to_np(lse[heads][:, gr]) - ref["lse"])))
     e_q = rel_fro(to_np(dq[gr][:, heads]), ref["dq"])
-    _say(f"[parity] over-2GiB: o {e_o:.3e}, lse {e_l:.3e}, dq rel-fro {e_q:.3e}")
+    _say(f"[parity] over-4GiB: o {e_o:.3e}, lse {e_l:.3e}, dq rel-fro {e_q:.3e}")
     assert e_o <= 2e-2 and e_l <= 1e-3 and e_q <= 1e-2
     krows = [P - 2, P - 1, P, P + 100, P + R - 1]
     kref = repeated_prefix_key_rows(one, sub["q"], sub["k"], sub["v"], sub["do"], krows, [0, 7])
     gk = [g0 + r for r in krows]
     e_k = rel_fro(to_np(dk[gk][:, [0, 7]]), kref["dk"])
     e_v = rel_fro(to_np(dv[gk][:, [0, 7]]), kref["dv"])
-    _say(f"[parity] over-2GiB: dk rel-fro {e_k:.3e}, dv rel-fro {e_v:.3e}")
+    _say(f"[parity] over-4GiB: dk rel-fro {e_k:.3e}, dv rel-fro {e_v:.3e}")
     assert e_k <= 1e-2 and e_v <= 1e-2
