@@ -80,6 +80,8 @@ def parse(argv=None):
                     help="bf16_gqa_g16_p8192 (default), or bf16_scoring_p32768 with --forward-only")
     ap.add_argument("--ratio-sweep", action="store_true",
                     help="time grouped vs repeated-prefix layouts over prefix/response ratios")
+    ap.add_argument("--ratios", default="0.5,1,2,4,8,16,32,64",
+                    help="prefix/response ratios of --ratio-sweep (comma-separated)")
     ap.add_argument("--forward-only", action="store_true",
                     help="score without backward and without storing the logsumexp")
     ap.add_argument("--decoder", action="store_true",
@@ -233,9 +235,29 @@ def path_bytes(T, hq, hkv, d, esize=2):
     return 4 * T * hq * d * esize + 4 * T * hkv * d * esize + 3 * hq * T * 4
 
 
+def steady_ms(run, torch, target_ms=20.0):
+    """Mean step time of a Runner over about target_ms of back-to-back steps
+    (after a short warm-up), timed with two events on the current stream."""
+    for _ in range(3):
+        run.step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run.step()
+    torch.cuda.synchronize()
+    est = max((time.perf_counter() - t0) * 1e3, 0.05)
+    n = int(min(2000, max(10, target_ms / est)))
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(n):
+        run.step()
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / n
+
+
 def ratio_sweep(a, pg, torch) -> dict:
     G, R, hq, hkv, d = 16, 256, 32, 8, 128
-    ratios = [0.5, 1, 2, 4, 8, 16, 32, 64]
+    ratios = [float(x) if "." in x else int(x) for x in a.ratios.split(",")]
     gen = torch.Generator(device="cuda").manual_seed(7)
     points = []
     # one untimed pass of the first layout: loading the library's code objects
@@ -257,7 +279,8 @@ def ratio_sweep(a, pg, torch) -> dict:
         base_mem = torch.cuda.memory_allocated()
         torch.cuda.reset_peak_memory_stats()
         run = Runner(pg, torch, groups, w, tens)
-        g_ms, _, _ = run.timed(max(2, a.steps // 4), 2)
+        run.step()
+        torch.cuda.synchronize()
         # inputs + outputs + workspace + plan of the step
         g_peak = torch.cuda.max_memory_allocated() - base_mem + sum(x.numel() * x.element_size() for x in tens)
         pairs, base_pairs = run.batch.pairs, run.batch.baseline_pairs
@@ -265,14 +288,22 @@ def ratio_sweep(a, pg, torch) -> dict:
                               for i in range(G)])
         idx_t = torch.from_numpy(idx).to("cuda")
         btens = [x.index_select(0, idx_t).contiguous() for x in tens]
-        del run
         torch.cuda.synchronize()
         base_mem = torch.cuda.memory_allocated()
         torch.cuda.reset_peak_memory_stats()
         brun = Runner(pg, torch, [(P, [R])] * G, w, btens)
-        b_ms, _, _ = brun.timed(max(2, a.steps // 4), 1)
+        brun.step()
+        torch.cuda.synchronize()
         b_peak = torch.cuda.max_memory_allocated() - base_mem + sum(x.numel() * x.element_size() for x in btens)
-        del brun, btens, tens
+        # Steps of a fraction of a millisecond: each layout is timed over about
+        # 20 ms of steps without the per-kernel timing events (whose records
+        # would weigh in), three times alternately, and the medians are used.
+        g_runs, b_runs = [], []
+        for _ in range(3):
+            g_runs.append(steady_ms(run, torch))
+            b_runs.append(steady_ms(brun, torch))
+        g_ms, b_ms = float(np.median(g_runs)), float(np.median(b_runs))
+        del run, brun, btens, tens
         torch.cuda.empty_cache()
         pt = {"ratio": ratio, "prefix": P, "grouped_ms": round(g_ms, 4), "repeated_prefix_ms": round(b_ms, 4),
               "time_ratio": round(g_ms / b_ms, 4), "attn_flop_ratio": round(pairs / base_pairs, 4),

@@ -425,35 +425,54 @@ __global__ __launch_bounds__(512) void dkdv_bf16_kernel(
 }
 
 // Sum of the pieces of each cut key tile, in piece order, to bf16 dK / dV.
-// Block (s, hk, kind): kv_sums[s] = {k0, k1, first part, parts}; kind 0 is
-// dV, 1 is dK.  Each thread adds one 4-float chunk of a key row over the
-// parts.
+// kv_sums[s] = {k0, k1, first part, parts}.  A block adds SUM_ROWS key rows
+// (1024 floats) of one (cut tile, kv head, dV / dK): each thread one 4-float
+// chunk, over the parts in order.  The partials were just written by the
+// dK/dV kernel and are mostly L2-resident; with a block per 1024 floats the
+// sum spreads over the whole GPU even when a single tile was cut.
 template <int D>
 __global__ __launch_bounds__(256) void dkdv_sum_kernel(const int32_t *__restrict__ kv_sums,
                                                        const float *__restrict__ partial,
                                                        bf16 *__restrict__ dK,
                                                        bf16 *__restrict__ dV, int Hkv) {
   constexpr int BN = PG_TILE_KV, CH = D / 4;
-  const int kind = blockIdx.x & 1;
-  const int sh = blockIdx.x >> 1;
+  constexpr int SUM_ROWS = 1024 / D;            // key rows per block
+  constexpr int NRB = BN / SUM_ROWS;            // row blocks per tile
+  static_assert(SUM_ROWS * CH == 256, "one 4-float chunk per thread");
+  const int rb = blockIdx.x % NRB;
+  const int rest = blockIdx.x / NRB;
+  const int kind = rest & 1;
+  const int sh = rest >> 1;
   const int si = sh / Hkv, hk = sh - si * Hkv;
   const int k0 = kv_sums[4 * si + 0], k1 = kv_sums[4 * si + 1];
   const int first = kv_sums[4 * si + 2], np = kv_sums[4 * si + 3];
+  const int kl = rb * SUM_ROWS + (int)threadIdx.x / CH;  // key row within the tile
+  const int c = (int)threadIdx.x % CH;
+  if (k0 + kl >= k1) return;
   const size_t pstride = (size_t)Hkv * 2 * BN * D;
-  const float *base = partial + (((size_t)first * Hkv + hk) * 2 + kind) * (BN * D);
-  bf16 *out = kind == 0 ? dV : dK;
-  for (int i = threadIdx.x; i < (k1 - k0) * CH; i += 256) {
-    const int kl = i / CH, c = i - kl * CH;
-    const float *src = base + (size_t)kl * D + 4 * c;
-    f32x4 a = *reinterpret_cast<const f32x4 *>(src);
-    for (int j = 1; j < np; ++j) {
-      const f32x4 b = *reinterpret_cast<const f32x4 *>(src + j * pstride);
+  const float *src = partial + (((size_t)first * Hkv + hk) * 2 + kind) * (BN * D) +
+                     (size_t)kl * D + 4 * c;
+  // the parts' loads are issued eight at a time (the partials come from
+  // other XCDs' writes, a long round trip each), then added in part order
+  f32x4 a = *reinterpret_cast<const f32x4 *>(src);
+  int j = 1;
+  for (; j + 8 <= np; j += 8) {
+    f32x4 b[8];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) a[e] += b[e];
-    }
-    *reinterpret_cast<u32x2 *>(out + ((size_t)(k0 + kl) * Hkv + hk) * D + 4 * c) =
-        pack4_bf16(a[0], a[1], a[2], a[3]);
+    for (int u = 0; u < 8; ++u) b[u] = *reinterpret_cast<const f32x4 *>(src + (size_t)(j + u) * pstride);
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a[e] += b[u][e];
   }
+  for (; j < np; ++j) {
+    const f32x4 b = *reinterpret_cast<const f32x4 *>(src + (size_t)j * pstride);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) a[e] += b[e];
+  }
+  bf16 *out = kind == 0 ? dV : dK;
+  *reinterpret_cast<u32x2 *>(out + ((size_t)(k0 + kl) * Hkv + hk) * D + 4 * c) =
+      pack4_bf16(a[0], a[1], a[2], a[3]);
 }
 
 // ---------------------------------------------------------------- dQ
@@ -695,7 +714,8 @@ hipError_t launch_bwd_dkdv_bf16(const Plan &p, float scale, const void *q, const
                        sl2, scale);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_kv_sums == 0) return e;
-  const dim3 sgrid((unsigned)p.n_kv_sums * (unsigned)p.Hkv * 2u), sblock(256);
+  const unsigned nrb = PG_TILE_KV / (1024u / (unsigned)p.D);  // row blocks per cut tile
+  const dim3 sgrid((unsigned)p.n_kv_sums * (unsigned)p.Hkv * 2u * nrb), sblock(256);
   if (p.D == 128)
     hipLaunchKernelGGL(dkdv_sum_kernel<128>, sgrid, sblock, 0, s, p.kv_sums,
                        (const float *)partial, (bf16 *)dk, (bf16 *)dv, p.Hkv);
