@@ -307,16 +307,23 @@ pg_status pg_rope(const pg_desc *d, pg_dtype t, void *x, int32_t num_heads, int3
  * logits of the row before each response token in its baseline sequence
  * [P; R_i]; a response's first token is scored by the group's last prefix
  * row).  Logits are hidden @ weight^T (LM head without bias), bf16 operands,
- * fp32 accumulation; the products run as rocBLAS GEMMs, the rest in this
- * library's kernels.  hidden: bf16 [T, d_model] in packed order; weight:
- * bf16 [vocab, d_model]; tokens: int32 [T] token id of every packed row
+ * fp32 accumulation.  The logits are computed in this library's MFMA tile
+ * kernels and reduced in place (forward: per-row max, sum of exponentials
+ * and target logit per 256-entry vocab tile; backward: the gradient of the
+ * logits, stored as bf16), so they are never written to memory; the
+ * backward's two products dH = G weight and dW = G^T H run as rocBLAS GEMMs.
+ * hidden: bf16 [T, d_model] in packed order; weight: bf16 [vocab, d_model]
+ * (under 4 GiB, as are the num_scored gathered hidden rows: larger heads
+ * return PG_ERR_UNSUPPORTED); tokens: int32 [T] token id of every packed row
  * (read only at scored rows; an id outside [0, vocab) gives logp = NaN).
  * d_model a multiple of 8.  Device buffers, 16-byte aligned, caller-owned. */
 
-/* Bytes of scratch pg_logprob_fwd / pg_logprob_bwd need: the logits of the
- * scored rows (fp32 [num_scored, vocab]), their gradient (bf16, same shape),
- * the gathered predicting rows (bf16) and their gradient (fp32
- * [num_scored, d_model]), 256-byte aligned.  0 if the arguments are invalid. */
+/* Bytes of scratch pg_logprob_fwd / pg_logprob_bwd need: the gradient of the
+ * logits (bf16 [num_scored, vocab]), the gathered predicting rows (bf16
+ * [num_scored, d_model]) and their gradient (fp32), the forward's per-tile
+ * row max and sum (fp32 [ceil(vocab / 256), num_scored] each) and target
+ * logits (fp32 [num_scored]), each 256-byte aligned.  0 if the arguments are
+ * invalid. */
 size_t pg_logprob_workspace_size(const pg_desc *d, int32_t vocab, int32_t d_model);
 
 /* logp [num_scored]: log-probability of each scored token; lse

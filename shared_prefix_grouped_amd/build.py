@@ -26,7 +26,7 @@ ARCH = "gfx950"
 EXTRA: list = []  # e.g. ["-Rpass-analysis=kernel-resource-usage"] to print register use
 
 SOURCES = ["pg_api.cpp", "pg_fwd_bf16.hip", "pg_bwd_bf16.hip", "pg_f32.hip", "pg_rows.hip",
-           "pg_head.hip"]
+           "pg_head.hip", "pg_head_mfma.hip"]
 
 # Packed-fp32 VALU instructions are switched off for all device code: the
 # compiler otherwise forms v_pk_{add,mul,fma}_f32 from plain float code.

@@ -612,18 +612,23 @@ pg_status get_blas(Blas &b, rocblas_handle *out) {  // b.mu held
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// Workspace of the head: logits Z [n, V] fp32, G [n, V] bf16, H_pred [n, dm]
-// bf16, dH_pred [n, dm] fp32.
+// Workspace of the head: G [n, V] bf16 (the gradient of the loss with
+// respect to the logits), H_pred [n, dm] bf16, dH_pred [n, dm] fp32, and the
+// forward's per-vocab-tile row max and sum ([nvt, n] fp32 each) and target
+// logits ([n] fp32).  The logits themselves are never stored.
 struct HeadWs {
-  size_t z, g, hp, dhp, total;
+  size_t g, hp, dhp, pm, ps, zt, total;
 };
 HeadWs head_ws(int64_t n, int64_t V, int64_t dm) {
   HeadWs w{};
-  w.z = 0;
-  w.g = align256(w.z + size_t(n) * V * 4);
+  const size_t nvt = size_t(pg::head_vocab_tiles(int(V)));
+  w.g = 0;
   w.hp = align256(w.g + size_t(n) * V * 2);
   w.dhp = align256(w.hp + size_t(n) * dm * 2);
-  w.total = std::max<size_t>(256, align256(w.dhp + size_t(n) * dm * 4));
+  w.pm = align256(w.dhp + size_t(n) * dm * 4);
+  w.ps = align256(w.pm + nvt * size_t(n) * 4);
+  w.zt = align256(w.ps + nvt * size_t(n) * 4);
+  w.total = std::max<size_t>(256, align256(w.zt + size_t(n) * 4));
   return w;
 }
 
@@ -632,6 +637,10 @@ pg_status check_head(const pg_desc *d, int32_t vocab, int32_t d_model) {
   if (st != PG_OK) return st;
   if (vocab < 1 || d_model < 8 || d_model % 8)
     return fail(PG_ERR_INVALID_ARG, "vocab must be >= 1 and d_model a positive multiple of 8");
+  // the tile kernels address W and H_pred with 32-bit byte offsets
+  if (int64_t(vocab) * d_model * 2 >= (int64_t(1) << 32) ||
+      int64_t(d->num_scored) * d_model * 2 >= (int64_t(1) << 32))
+    return fail(PG_ERR_UNSUPPORTED, "weight and scored hidden rows must each be under 4 GiB");
   if (d->num_scored < 0 || d->num_resp < 0)
     return fail(PG_ERR_INVALID_ARG, "descriptor is not one filled by pg_pack");
   if (d->num_scored > 0 && (!d->scored_row || !d->scored_pred || !d->scored_resp ||
@@ -640,17 +649,9 @@ pg_status check_head(const pg_desc *d, int32_t vocab, int32_t d_model) {
   return PG_OK;
 }
 
-// The row-major products of the head, in rocBLAS terms:
-//   Z [n, V]  = H_pred [n, dm] W^T        -> (T, N): m = V,  n = n,  k = dm
+// The row-major backward products of the head, in rocBLAS terms:
 //   dH [n, dm] = G [n, V] W [V, dm]       -> (N, N): m = dm, n = n,  k = V
 //   dW [V, dm] = G^T H_pred               -> (N, T): m = dm, n = V,  k = n
-pg_status head_logits(rocblas_handle h, const void *hp, const void *weight, float *z, int n, int V,
-                      int dm) {
-  return blas_status(gemm_bf16(h, rocblas_operation_transpose, rocblas_operation_none, V, n, dm,
-                               weight, dm, hp, dm, z, V),
-                     "logits GEMM");
-}
-
 
 // ---------------------------------------------------------------- plan upload staging
 // pg_pack writes the plan into a pinned, device-mapped host buffer that the
@@ -1023,22 +1024,16 @@ pg_status pg_logprob_fwd(const pg_desc *d, const void *hidden, const void *weigh
     return fail(PG_ERR_WORKSPACE, "workspace too small: need " + std::to_string(w.total) +
                                       " bytes, got " + std::to_string(ws_bytes));
   char *ws = static_cast<char *>(workspace);
-  float *z = reinterpret_cast<float *>(ws + w.z);
   void *hp = ws + w.hp;
+  float *pm = reinterpret_cast<float *>(ws + w.pm), *ps = reinterpret_cast<float *>(ws + w.ps);
+  float *zt = reinterpret_cast<float *>(ws + w.zt);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  Blas &b = blas();
-  std::lock_guard<std::mutex> lock(b.mu);
-  rocblas_handle h;
-  if ((st = get_blas(b, &h)) != PG_OK) return st;
-  if ((st = blas_status(rocblas_set_stream(h, s), "rocblas_set_stream")) != PG_OK) return st;
-  pg_status gst = PG_OK;
   hipError_t e = timed(PG_KERNEL_HEAD_FWD, s, [&] {
     hipError_t r = pg::launch_gather_rows(d->scored_pred, hidden, hp, n, d_model, s);
     if (r != hipSuccess) return r;
-    if ((gst = head_logits(h, hp, weight, z, n, vocab, d_model)) != PG_OK) return hipErrorUnknown;
-    return pg::launch_lsm_fwd(z, d->scored_row, tokens, logp, lse, n, vocab, s);
+    return pg::launch_head_logprob(hp, weight, d->scored_row, tokens, pm, ps, zt, logp, lse, n,
+                                   vocab, d_model, s);
   });
-  if (gst != PG_OK) return gst;
   return hip_status(e, "pg_logprob_fwd launch");
 }
 
@@ -1077,7 +1072,6 @@ pg_status pg_logprob_bwd(const pg_desc *d, const void *hidden, const void *weigh
     return fail(PG_ERR_WORKSPACE, "workspace too small: need " + std::to_string(w.total) +
                                       " bytes, got " + std::to_string(ws_bytes));
   char *ws = static_cast<char *>(workspace);
-  float *z = reinterpret_cast<float *>(ws + w.z);
   void *g = ws + w.g;
   void *hp = ws + w.hp;
   float *dhp = reinterpret_cast<float *>(ws + w.dhp);
@@ -1093,9 +1087,8 @@ pg_status pg_logprob_bwd(const pg_desc *d, const void *hidden, const void *weigh
     if (n > 0) {
       if ((r = pg::launch_gather_rows(d->scored_pred, hidden, hp, n, d_model, s)) != hipSuccess)
         return r;
-      if ((gst = head_logits(h, hp, weight, z, n, vocab, d_model)) != PG_OK) return hipErrorUnknown;
-      if ((r = pg::launch_lsm_bwd(z, d->scored_row, tokens, lse, dlogp, g, n, vocab, s)) !=
-          hipSuccess)
+      if ((r = pg::launch_head_grad(hp, weight, d->scored_row, tokens, lse, dlogp, g, n, vocab,
+                                    d_model, s)) != hipSuccess)
         return r;
       if ((gst = blas_status(gemm_bf16(h, rocblas_operation_none, rocblas_operation_none, d_model,
                                        n, vocab, weight, d_model, g, vocab, dhp, d_model),

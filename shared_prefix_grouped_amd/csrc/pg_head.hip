@@ -6,15 +6,11 @@
 // Only the scored rows are computed: the predicting row of every response
 // token (the previous position of its baseline sequence; a response's first
 // token is scored by the group's last prefix row, shared by the G responses).
-// The logits Z = H_pred W^T and the two backward products are plain GEMMs
-// (rocBLAS, bf16 operands, fp32 accumulation); the kernels here are the
-// memory-bound steps around them:
+// The logits products and the log-softmax around them are the tile kernels of
+// pg_head_mfma.hip; the kernels here are the row moves and the loss:
 //   gather_rows   H_pred[k] = hidden[pred[k]]
-//   lsm_fwd       per scored row: logsumexp over the vocabulary (one pass,
-//                 running max) and logp = z[token] - lse
 //   grpo_loss     loss = -mean_i(A_i * S_i), S_i = sum of response i's logp,
 //                 summed entry by entry; dlogp[k] = -A_{resp(k)} / n_resp
-//   lsm_bwd       G[k, v] = dlogp[k] * ([v == token] - exp(z[k, v] - lse[k]))
 //   scatter_rows  dhidden[t] = sum of dH_pred[k] over the entries t predicts,
 //                 in entry order (the last prefix row of a group sums its G
 //                 responses' first tokens: the prefix gradient is the sum of
@@ -36,59 +32,6 @@ __global__ __launch_bounds__(kHeadThreads) void gather_rows_kernel(
   if (i >= (long long)n * cpr) return;
   const int k = (int)(i / cpr), c = (int)(i - (long long)k * cpr);
   out[i] = hidden[(size_t)pred[k] * cpr + c];
-}
-
-// Block reduction of (max, sum of exp(x - max)) pairs, fixed tree order.
-__device__ __forceinline__ void combine(float &m, float &s, float m2, float s2) {
-  const float mn = fmaxf(m, m2);
-  s = (m == -INFINITY ? 0.f : s * __expf(m - mn)) + (m2 == -INFINITY ? 0.f : s2 * __expf(m2 - mn));
-  m = mn;
-}
-
-template <bool kVec4>
-__global__ __launch_bounds__(kHeadThreads) void lsm_fwd_kernel(
-    const float *__restrict__ z, const int32_t *__restrict__ scored_row,
-    const int32_t *__restrict__ tokens, float *__restrict__ logp, float *__restrict__ lse, int V) {
-  const int k = blockIdx.x, tid = threadIdx.x;
-  const float *row = z + (size_t)k * V;
-  float m = -INFINITY, s = 0.f;
-  if (kVec4) {
-    const float4 *r4 = reinterpret_cast<const float4 *>(row);
-    for (int i = tid; i < V / 4; i += kHeadThreads) {
-      const float4 x = r4[i];
-      const float xm = fmaxf(fmaxf(x.x, x.y), fmaxf(x.z, x.w));
-      const float mn = fmaxf(m, xm);
-      s = (m == -INFINITY ? 0.f : s * __expf(m - mn)) + __expf(x.x - mn) + __expf(x.y - mn) +
-          __expf(x.z - mn) + __expf(x.w - mn);
-      m = mn;
-    }
-  } else {
-    for (int i = tid; i < V; i += kHeadThreads) {
-      const float x = row[i];
-      const float mn = fmaxf(m, x);
-      s = (m == -INFINITY ? 0.f : s * __expf(m - mn)) + __expf(x - mn);
-      m = mn;
-    }
-  }
-  __shared__ float sm[kHeadThreads], ss[kHeadThreads];
-  sm[tid] = m;
-  ss[tid] = s;
-  __syncthreads();
-  for (int w = kHeadThreads / 2; w > 0; w >>= 1) {
-    if (tid < w) {
-      float a = sm[tid], b = ss[tid];
-      combine(a, b, sm[tid + w], ss[tid + w]);
-      sm[tid] = a;
-      ss[tid] = b;
-    }
-    __syncthreads();
-  }
-  if (tid == 0) {
-    const float l = sm[0] + __logf(ss[0]);
-    lse[k] = l;
-    const int tok = tokens[scored_row[k]];
-    logp[k] = (unsigned)tok < (unsigned)V ? row[tok] - l : __int_as_float(0x7fc00000);  // NaN: bad id
-  }
 }
 
 // One block: loss = -(1/n_resp) sum_r A_r S_r = -(1/n_resp) sum_k A_{resp(k)} logp_k,
@@ -113,33 +56,6 @@ __global__ __launch_bounds__(kHeadThreads) void grpo_dlogp_kernel(
     float *__restrict__ dlogp, int n, int n_resp) {
   const int k = blockIdx.x * kHeadThreads + threadIdx.x;
   if (k < n) dlogp[k] = -adv[scored_resp[k]] / (float)n_resp;
-}
-
-template <bool kVec4>
-__global__ __launch_bounds__(kHeadThreads) void lsm_bwd_kernel(
-    const float *__restrict__ z, const int32_t *__restrict__ scored_row,
-    const int32_t *__restrict__ tokens, const float *__restrict__ lse,
-    const float *__restrict__ dlogp, bf16 *__restrict__ g, int V) {
-  const int k = blockIdx.x, tid = threadIdx.x;
-  const float *row = z + (size_t)k * V;
-  bf16 *grow = g + (size_t)k * V;
-  const float l = lse[k], d = dlogp[k];
-  const int tok = tokens[scored_row[k]];
-  if (kVec4) {
-    const float4 *r4 = reinterpret_cast<const float4 *>(row);
-    for (int i = tid; i < V / 4; i += kHeadThreads) {
-      const float4 x = r4[i];
-      const int v = 4 * i;
-      const float g0 = d * ((v + 0 == tok ? 1.f : 0.f) - __expf(x.x - l));
-      const float g1 = d * ((v + 1 == tok ? 1.f : 0.f) - __expf(x.y - l));
-      const float g2 = d * ((v + 2 == tok ? 1.f : 0.f) - __expf(x.z - l));
-      const float g3 = d * ((v + 3 == tok ? 1.f : 0.f) - __expf(x.w - l));
-      *reinterpret_cast<u32x2 *>(grow + v) = pack4_bf16(g0, g1, g2, g3);
-    }
-  } else {
-    for (int v = tid; v < V; v += kHeadThreads)
-      grow[v] = (bf16)(d * ((v == tok ? 1.f : 0.f) - __expf(row[v] - l)));
-  }
 }
 
 __global__ __launch_bounds__(kHeadThreads) void scatter_rows_kernel(
@@ -172,18 +88,6 @@ hipError_t launch_gather_rows(const int32_t *pred, const void *hidden, void *out
   return hipGetLastError();
 }
 
-hipError_t launch_lsm_fwd(const float *z, const int32_t *scored_row, const int32_t *tokens,
-                          float *logp, float *lse, int n, int V, hipStream_t s) {
-  if (n == 0) return hipSuccess;
-  if (V % 4 == 0)
-    hipLaunchKernelGGL(lsm_fwd_kernel<true>, dim3(n), dim3(kHeadThreads), 0, s, z, scored_row,
-                       tokens, logp, lse, V);
-  else
-    hipLaunchKernelGGL(lsm_fwd_kernel<false>, dim3(n), dim3(kHeadThreads), 0, s, z, scored_row,
-                       tokens, logp, lse, V);
-  return hipGetLastError();
-}
-
 hipError_t launch_grpo_loss(const float *logp, const int32_t *scored_resp, const float *adv,
                             float *loss, float *dlogp, int n, int n_resp, hipStream_t s) {
   hipLaunchKernelGGL(grpo_loss_kernel, dim3(1), dim3(kHeadThreads), 0, s, logp, scored_resp, adv,
@@ -192,19 +96,6 @@ hipError_t launch_grpo_loss(const float *logp, const int32_t *scored_resp, const
   if (e != hipSuccess || n == 0) return e;
   hipLaunchKernelGGL(grpo_dlogp_kernel, dim3(blocks_for(n)), dim3(kHeadThreads), 0, s,
                      scored_resp, adv, dlogp, n, n_resp);
-  return hipGetLastError();
-}
-
-hipError_t launch_lsm_bwd(const float *z, const int32_t *scored_row, const int32_t *tokens,
-                          const float *lse, const float *dlogp, void *g, int n, int V,
-                          hipStream_t s) {
-  if (n == 0) return hipSuccess;
-  if (V % 4 == 0)
-    hipLaunchKernelGGL(lsm_bwd_kernel<true>, dim3(n), dim3(kHeadThreads), 0, s, z, scored_row,
-                       tokens, lse, dlogp, (bf16 *)g, V);
-  else
-    hipLaunchKernelGGL(lsm_bwd_kernel<false>, dim3(n), dim3(kHeadThreads), 0, s, z, scored_row,
-                       tokens, lse, dlogp, (bf16 *)g, V);
   return hipGetLastError();
 }
 

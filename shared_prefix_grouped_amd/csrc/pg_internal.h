@@ -73,16 +73,24 @@ hipError_t launch_upload(const void *src_dev, void *dst, size_t bytes, const voi
 hipError_t launch_rows(const Plan &p, bool pack, void *packed, void *pre, void *resp,
                        size_t row_bytes, hipStream_t s);
 
-// Log-probability head kernels (the GEMMs around them are rocBLAS calls).
+// Log-probability head kernels.  The logits products run in this library's
+// MFMA tile kernels with the log-softmax in their epilogue; dH = G W and
+// dW = G^T H_pred are rocBLAS calls.
 hipError_t launch_gather_rows(const int32_t *pred, const void *hidden, void *out, int n,
                               int d_model, hipStream_t s);
-hipError_t launch_lsm_fwd(const float *z, const int32_t *scored_row, const int32_t *tokens,
-                          float *logp, float *lse, int n, int V, hipStream_t s);
+// number of 256-entry vocab tiles (rows of the per-tile max / sum arrays)
+int head_vocab_tiles(int V);
+// logp and lse of the n scored rows; part_m / part_s: [head_vocab_tiles(V), n]
+// floats, ztok: [n] floats of scratch
+hipError_t launch_head_logprob(const void *hp, const void *w, const int32_t *scored_row,
+                               const int32_t *tokens, float *part_m, float *part_s, float *ztok,
+                               float *logp, float *lse, int n, int V, int dm, hipStream_t s);
+// G [n, V] bf16, the gradient of the loss with respect to the logits
+hipError_t launch_head_grad(const void *hp, const void *w, const int32_t *scored_row,
+                            const int32_t *tokens, const float *lse, const float *dlogp, void *g,
+                            int n, int V, int dm, hipStream_t s);
 hipError_t launch_grpo_loss(const float *logp, const int32_t *scored_resp, const float *adv,
                             float *loss, float *dlogp, int n, int n_resp, hipStream_t s);
-hipError_t launch_lsm_bwd(const float *z, const int32_t *scored_row, const int32_t *tokens,
-                          const float *lse, const float *dlogp, void *g, int n, int V,
-                          hipStream_t s);
 hipError_t launch_scatter_rows(const int32_t *pred_start, const int32_t *pred_list,
                                const float *dh_pred, float *dhidden, int T, int d_model,
                                hipStream_t s);

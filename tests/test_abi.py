@@ -353,13 +353,20 @@ def test_head_sizes_and_validation():
     assert desc.num_scored == 9
     n, V, dm = 9, 1000, 64
     a256 = lambda x: -(-x // 256) * 256
-    z = n * V * 4
-    g = a256(z) + n * V * 2
+    nvt = -(-V // 256)  # vocab tiles of the logits kernels
+    g = n * V * 2  # gradient of the logits, bf16; the logits are never stored
     hp = a256(g) + n * dm * 2
-    want = a256(a256(hp) + n * dm * 4)
+    dhp = a256(hp) + n * dm * 4
+    pm = a256(dhp) + nvt * n * 4
+    ps = a256(pm) + nvt * n * 4
+    zt = a256(ps) + n * 4
+    want = a256(zt)
     assert L.pg_logprob_workspace_size(ctypes.byref(desc), V, dm) == want
     assert L.pg_logprob_workspace_size(ctypes.byref(desc), 0, dm) == 0
     assert L.pg_logprob_workspace_size(ctypes.byref(desc), V, 12) == 0
+    # the logits kernels address W with 32-bit byte offsets: a 4 GiB head is refused
+    assert L.pg_logprob_workspace_size(ctypes.byref(desc), 1 << 20, 2048) == 0
+    assert L.pg_logprob_workspace_size(ctypes.byref(desc), (1 << 20) - 1, 2048) > 0
     p = ctypes.c_void_p(4096)
     assert L.pg_logprob_fwd(ctypes.byref(desc), p, p, V, dm, p, p, p, p, want - 1,
                             None) == pg.PG_ERR_WORKSPACE
