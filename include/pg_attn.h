@@ -308,9 +308,10 @@ pg_status pg_rope(const pg_desc *d, pg_dtype t, void *x, int32_t num_heads, int3
  * [P; R_i]; a response's first token is scored by the group's last prefix
  * row).  Logits are hidden @ weight^T (LM head without bias), bf16 operands,
  * fp32 accumulation.  The logits are computed in this library's MFMA tile
- * kernels and reduced in place (forward: per-row max, sum of exponentials
- * and target logit per 256-entry vocab tile; backward: the gradient of the
- * logits, stored as bf16), so they are never written to memory; the
+ * kernels and reduced in place (forward: per-row max and sum of exponentials
+ * per 256-entry vocab tile, and the target logit as one dot product;
+ * backward: the gradient of the logits, stored as bf16), so they are never
+ * written to memory; the
  * backward's two products dH = G weight and dW = G^T H run as rocBLAS GEMMs.
  * hidden: bf16 [T, d_model] in packed order; weight: bf16 [vocab, d_model]
  * (under 4 GiB, as are the num_scored gathered hidden rows: larger heads
@@ -320,10 +321,9 @@ pg_status pg_rope(const pg_desc *d, pg_dtype t, void *x, int32_t num_heads, int3
 
 /* Bytes of scratch pg_logprob_fwd / pg_logprob_bwd need: the gradient of the
  * logits (bf16 [num_scored, vocab]), the gathered predicting rows (bf16
- * [num_scored, d_model]) and their gradient (fp32), the forward's per-tile
- * row max and sum (fp32 [ceil(vocab / 256), num_scored] each) and target
- * logits (fp32 [num_scored]), each 256-byte aligned.  0 if the arguments are
- * invalid. */
+ * [num_scored, d_model]) and their gradient (fp32), and the forward's
+ * per-tile row max and sum (fp32 [ceil(vocab / 256), num_scored] each), each
+ * 256-byte aligned.  0 if the arguments are invalid. */
 size_t pg_logprob_workspace_size(const pg_desc *d, int32_t vocab, int32_t d_model);
 
 /* logp [num_scored]: log-probability of each scored token; lse

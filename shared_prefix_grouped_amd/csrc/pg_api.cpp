@@ -614,10 +614,10 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Workspace of the head: G [n, V] bf16 (the gradient of the loss with
 // respect to the logits), H_pred [n, dm] bf16, dH_pred [n, dm] fp32, and the
-// forward's per-vocab-tile row max and sum ([nvt, n] fp32 each) and target
-// logits ([n] fp32).  The logits themselves are never stored.
+// forward's per-vocab-tile row max and sum ([nvt, n] fp32 each).  The logits
+// themselves are never stored.
 struct HeadWs {
-  size_t g, hp, dhp, pm, ps, zt, total;
+  size_t g, hp, dhp, pm, ps, total;
 };
 HeadWs head_ws(int64_t n, int64_t V, int64_t dm) {
   HeadWs w{};
@@ -627,8 +627,7 @@ HeadWs head_ws(int64_t n, int64_t V, int64_t dm) {
   w.dhp = align256(w.hp + size_t(n) * dm * 2);
   w.pm = align256(w.dhp + size_t(n) * dm * 4);
   w.ps = align256(w.pm + nvt * size_t(n) * 4);
-  w.zt = align256(w.ps + nvt * size_t(n) * 4);
-  w.total = std::max<size_t>(256, align256(w.zt + size_t(n) * 4));
+  w.total = std::max<size_t>(256, align256(w.ps + nvt * size_t(n) * 4));
   return w;
 }
 
@@ -1026,12 +1025,11 @@ pg_status pg_logprob_fwd(const pg_desc *d, const void *hidden, const void *weigh
   char *ws = static_cast<char *>(workspace);
   void *hp = ws + w.hp;
   float *pm = reinterpret_cast<float *>(ws + w.pm), *ps = reinterpret_cast<float *>(ws + w.ps);
-  float *zt = reinterpret_cast<float *>(ws + w.zt);
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = timed(PG_KERNEL_HEAD_FWD, s, [&] {
     hipError_t r = pg::launch_gather_rows(d->scored_pred, hidden, hp, n, d_model, s);
     if (r != hipSuccess) return r;
-    return pg::launch_head_logprob(hp, weight, d->scored_row, tokens, pm, ps, zt, logp, lse, n,
+    return pg::launch_head_logprob(hp, weight, d->scored_row, tokens, pm, ps, logp, lse, n,
                                    vocab, d_model, s);
   });
   return hip_status(e, "pg_logprob_fwd launch");

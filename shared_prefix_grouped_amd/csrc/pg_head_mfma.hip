@@ -7,10 +7,9 @@
 // One workgroup computes a 256 (vocab) x 256 (scored rows) tile of
 // Z^T = W H_pred^T with bf16 MFMAs and fp32 accumulation, and then
 //   forward:  per scored row, the tile's max and sum of exp(z - max) over its
-//             vocab entries, and the target logit z[token] when the token
-//             falls in the tile; a second kernel combines the per-tile
-//             (max, sum) pairs of a row in tile order into
-//             lse = max + log(sum) and logp = z[token] - lse;
+//             vocab entries; a second kernel combines the per-tile (max, sum)
+//             pairs of a row into lse = max + log(sum), computes the target
+//             logit z[token] as one dot product, and logp = z[token] - lse;
 //   backward: G[k, v] = dlogp[k] * ([v == token_k] - exp(z[k, v] - lse[k])),
 //             the gradient of the loss with respect to the logits, stored as
 //             bf16 for the two plain products dH = G W and dW = G^T H_pred.
@@ -21,6 +20,8 @@
 // partner in the other half of the wave); the row reductions are register
 // loops plus one exchange between the wave halves and one between the two
 // waves that share the rows.
+
+#include <type_traits>
 
 #include "pg_device.h"
 #include "pg_internal.h"
@@ -62,7 +63,6 @@ struct HeadTileArgs {
   const int32_t *scored_row;  // [n] target row of each scored entry
   const int32_t *tokens;      // [T] token ids of the packed rows
   float *part_m, *part_s;     // forward: [nvt, n] per-tile max and sum
-  float *ztok;                // forward: [n] target logit
   const float *lse, *dlogp;   // backward: [n]
   bf16 *g;                    // backward: [n, V]
 };
@@ -76,8 +76,8 @@ struct HeadTileArgs {
 // are fetched from chunk 0 of the block instead (in bounds; the fragments
 // they feed are zeroed before use).
 struct HeadCopy {
-  uint32_t off_w[8], off_h[8];  // byte offset of the lane's chunk, block 0
-  int chunk;                    // lane's source chunk in the block
+  uint32_t off[16];  // byte offset of the lane's chunk in block 0: W rows (k < 8), H_pred rows
+  int chunk;         // lane's source chunk in the block
 
   // (row % 16 = 8 (wave % 2) + lane / 8 for every k, so the chunk is one per lane)
   __device__ __forceinline__ void init(int v0, int m0, int V, int n, int dm, int wave, int lane) {
@@ -86,34 +86,43 @@ struct HeadCopy {
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const int row = (k * HWAVES + wave) * 8 + (lane >> 3);
-      off_w[k] = (uint32_t)min(v0 + row, V - 1) * rb + (uint32_t)(chunk * 16);
-      off_h[k] = (uint32_t)min(m0 + row, n - 1) * rb + (uint32_t)(chunk * 16);
+      off[k] = (uint32_t)min(v0 + row, V - 1) * rb + (uint32_t)(chunk * 16);
+      off[8 + k] = (uint32_t)min(m0 + row, n - 1) * rb + (uint32_t)(chunk * 16);
     }
   }
 
-  template <bool kTail>
-  __device__ __forceinline__ void issue(const bf16 *w, const bf16 *hp, int kb, int dm,
-                                        uint32_t lds_w, uint32_t lds_h, int wave) const {
-    // scalar 64-bit bases (uniform_ptr zero-extends the low word: readfirstlane
-    // returns int, and a sign-extended low word would corrupt the high one)
-    const uint64_t sw = (uint64_t)(uintptr_t)uniform_ptr(w + (size_t)kb * HK);
-    const uint64_t sh = (uint64_t)(uintptr_t)uniform_ptr(hp + (size_t)kb * HK);
-    // tail block: a chunk at or past d_model reads chunk 0 of the block
-    const uint32_t fix = (kTail && kb * HK + chunk * 8 >= dm) ? (uint32_t)(chunk * 16) : 0u;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const uint32_t a = lds_w + (uint32_t)((k * HWAVES + wave) * 1024);
-      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(a),
-                   "v"(off_w[k] - fix), "s"(sw)
-                   : "memory");
-    }
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const uint32_t a = lds_h + (uint32_t)((k * HWAVES + wave) * 1024);
-      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(a),
-                   "v"(off_h[k] - fix), "s"(sh)
-                   : "memory");
-    }
+  // Addresses of contraction block kb into the buffers at LDS byte addresses
+  // lw / lh.  Scalar 64-bit bases: uniform_ptr zero-extends the low word
+  // (readfirstlane returns int; a sign-extended low word would corrupt the
+  // high one).  In a block that d_model cuts, a chunk at or past d_model
+  // reads chunk 0 of the block instead.
+  struct Block {
+    uint64_t sw, sh;
+    uint32_t fix, lw, lh;
+  };
+  __device__ __forceinline__ Block block(const bf16 *w, const bf16 *hp, int kb, int dm,
+                                         uint32_t lw, uint32_t lh) const {
+    Block b;
+    b.sw = (uint64_t)(uintptr_t)uniform_ptr(w + (size_t)kb * HK);
+    b.sh = (uint64_t)(uintptr_t)uniform_ptr(hp + (size_t)kb * HK);
+    b.fix = kb * HK + chunk * 8 >= dm ? (uint32_t)(chunk * 16) : 0u;
+    b.lw = lw;
+    b.lh = lh;
+    return b;
+  }
+
+  // copy instruction k (0..15) of a block: 1 KB of W (k < 8) or of H_pred
+  template <int k>
+  __device__ __forceinline__ void one(const Block &b, int wave) const {
+    const uint32_t a = (k < 8 ? b.lw : b.lh) + (uint32_t)(((k & 7) * HWAVES + wave) * 1024);
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(a),
+                 "v"(off[k] - b.fix), "s"(k < 8 ? b.sw : b.sh)
+                 : "memory");
+  }
+  template <int k = 0>
+  __device__ __forceinline__ void all(const Block &b, int wave) const {
+    one<k>(b, wave);
+    if constexpr (k + 1 < 16) all<k + 1>(b, wave);
   }
 };
 
@@ -161,12 +170,15 @@ __global__ __launch_bounds__(HWAVES * 64) void head_tile_kernel(HeadTileArgs p, 
   struct Frags {
     bf16x8 a[4], b[4];
   };
-  // fragments of 16-deep step st of the block in buffer `cur`
+  // fragment i (0..7: A 0..3, B 0..3) of 16-deep step st of the block in buffer `cur`
+  auto frag = [&](uint32_t cur, int st, int i) {
+    return lds_frag((i < 4 ? tw0 : th0) + cur + (i & 3) * 32 * 128, foff[st]);
+  };
   auto load = [&](Frags &f, uint32_t cur, int st) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      f.a[i] = lds_frag(tw0 + cur + i * 32 * 128, foff[st]);
-      f.b[i] = lds_frag(th0 + cur + i * 32 * 128, foff[st]);
+      f.a[i] = frag(cur, st, i);
+      f.b[i] = frag(cur, st, 4 + i);
     }
   };
   auto mma = [&](const Frags &f) {
@@ -184,11 +196,29 @@ __global__ __launch_bounds__(HWAVES * 64) void head_tile_kernel(HeadTileArgs p, 
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
     }
   };
-  auto issue = [&](int kb, uint32_t buf) {
-    if (kb + 1 == nkb && tail)
-      cp.issue<true>(p.w, p.hp, kb, dm, lw + buf, lh + buf, wave);
-    else
-      cp.issue<false>(p.w, p.hp, kb, dm, lw + buf, lh + buf, wave);
+  // Step 3 of a block after the barrier, with the 16 copy instructions of
+  // block kb + 2 (if any) and the 8 fragment reads of the next block's step 0
+  // (if it is a whole block) placed one per MFMA: issued in one burst they
+  // would leave the MFMA pipe idle.  The MFMAs are unconditional (the
+  // accumulators take one path through the loop); only the copies and reads
+  // are.
+  auto step3 = [&](const Frags &f, Frags &g, const HeadCopy::Block &blk, bool cp_ok, bool rd_ok,
+                   uint32_t nxt) {
+#define PG_HEAD_SLOT(k)                                                                    \
+  acc[(k) >> 2][(k) & 3] = mfma32(f.a[(k) >> 2], f.b[(k) & 3], acc[(k) >> 2][(k) & 3]);    \
+  if (cp_ok) cp.one<k>(blk, wave);                                                         \
+  if (((k) & 1) && rd_ok) {                                                                \
+    constexpr int i = (k) >> 1;                                                            \
+    if (i < 4)                                                                             \
+      g.a[i & 3] = frag(nxt, 0, i);                                                        \
+    else                                                                                   \
+      g.b[i & 3] = frag(nxt, 0, i);                                                        \
+  }
+    PG_HEAD_SLOT(0) PG_HEAD_SLOT(1) PG_HEAD_SLOT(2) PG_HEAD_SLOT(3)
+    PG_HEAD_SLOT(4) PG_HEAD_SLOT(5) PG_HEAD_SLOT(6) PG_HEAD_SLOT(7)
+    PG_HEAD_SLOT(8) PG_HEAD_SLOT(9) PG_HEAD_SLOT(10) PG_HEAD_SLOT(11)
+    PG_HEAD_SLOT(12) PG_HEAD_SLOT(13) PG_HEAD_SLOT(14) PG_HEAD_SLOT(15)
+#undef PG_HEAD_SLOT
   };
 
   // Whole 64-deep blocks, two in flight: block kb + 2 is copied into the
@@ -196,9 +226,9 @@ __global__ __launch_bounds__(HWAVES * 64) void head_tile_kernel(HeadTileArgs p, 
   // registers (the barrier between its steps 2 and 3), and block kb + 1's
   // first fragments are read while step 3 of block kb multiplies.
   const int nfull = dm / HK;
-  issue(0, 0);
+  cp.all(cp.block(p.w, p.hp, 0, dm, lw, lh), wave);
   if (nkb > 1) {
-    issue(1, BUF);
+    cp.all(cp.block(p.w, p.hp, 1, dm, lw + BUF, lh + BUF), wave);
     // each wave issues 16 copies per block: vmcnt(16) waits for block 0's
     // and leaves block 1's in flight
     __builtin_amdgcn_s_waitcnt(0x0F70 | (1 << 14));
@@ -221,10 +251,8 @@ __global__ __launch_bounds__(HWAVES * 64) void head_tile_kernel(HeadTileArgs p, 
     interleave();
     wait_async_loads();
     __syncthreads();  // block kb + 1 is in LDS; block kb's reads are done
-    if (kb + 2 < nkb) issue(kb + 2, cur);
-    if (kb + 1 < nfull) load(f0, nxt, 0);
-    mma(f1);
-    if (kb + 1 < nfull) interleave();
+    step3(f1, f0, cp.block(p.w, p.hp, kb + 2, dm, lw + cur, lh + cur), kb + 2 < nkb,
+          kb + 1 < nfull, nxt);
   }
   if (tail) {
     // the last, partial block (in LDS since the last barrier): steps past
@@ -250,50 +278,55 @@ __global__ __launch_bounds__(HWAVES * 64) void head_tile_kernel(HeadTileArgs p, 
 
   // vocab entry of register r of block a in this lane: vb + 32 a + mfma_row(r, hi)
   const int vb = v0 + wv * 128;
-  const bool vfull = v0 + HT <= p.V;
-
   if constexpr (EPI == 0) {
+    // per scored row of the wave: max and sum of exp(z - max) over its 128
+    // vocab entries (64 in the lane, 64 in its partner in the other half of
+    // the wave); with kMask, entries past the vocabulary (the last vocab
+    // tile) take no part, and a slab wholly past it gives max -inf, sum 0
+    auto rows = [&](auto mask_tag) {
+      constexpr bool kMask = decltype(mask_tag)::value;
+      auto val = [&](int a, int b, int r) {
+        const float z = acc[a][b][r];
+        if constexpr (kMask) return vb + 32 * a + mfma_row(r, hi) < p.V ? z : -INFINITY;
+        return z;
+      };
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int rl = wm * 128 + b * 32 + l32;  // row inside the tile
-      const int row = m0 + rl;
-      const bool rok = row < p.n;
-      const int tok = rok ? p.tokens[p.scored_row[row]] : -1;
-      float mx = -INFINITY, zt = 0.f;
-      bool has = false;
+      for (int b = 0; b < 4; ++b) {
+        float m4[4];
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
+        for (int a = 0; a < 4; ++a) {
+          float x = val(a, b, 0);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int v = vb + 32 * a + mfma_row(r, hi);
-          const float z = acc[a][b][r];
-          if (vfull || v < p.V) mx = fmaxf(mx, z);
-          if (v == tok) {
-            zt = z;
-            has = true;
-          }
+          for (int r = 1; r < 16; ++r) x = fmaxf(x, val(a, b, r));
+          m4[a] = x;
         }
-      float lo, up;
-      wave_halves(mx, lo, up);
-      mx = fmaxf(lo, up);
-      const float ml = mx * kLog2e;
-      float s = 0.f;
+        float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
+        float lo, up;
+        wave_halves(mx, lo, up);
+        mx = fmaxf(lo, up);
+        const float ml = mx == -INFINITY ? 0.f : mx * kLog2e;
+        float s4[4];
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
+        for (int a = 0; a < 4; ++a) {
+          float x = 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int v = vb + 32 * a + mfma_row(r, hi);
-          const float e = fast_exp2(fmaf(acc[a][b][r], kLog2e, -ml));
-          if (vfull || v < p.V) s += e;
+          for (int r = 0; r < 16; ++r) x += fast_exp2(fmaf(val(a, b, r), kLog2e, -ml));
+          s4[a] = x;
         }
-      wave_halves(s, lo, up);
-      s = lo + up;
-      if (hi == 0) {
-        red_m[wv][rl] = mx;
-        red_s[wv][rl] = s;
+        float sum = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+        wave_halves(sum, lo, up);
+        sum = lo + up;
+        const int rl = wm * 128 + b * 32 + l32;  // row inside the tile
+        if (hi == 0) {
+          red_m[wv][rl] = mx;
+          red_s[wv][rl] = sum;
+        }
       }
-      if (has && rok) p.ztok[row] = zt;
-    }
+    };
+    if (v0 + HT <= p.V)
+      rows(std::false_type{});
+    else
+      rows(std::true_type{});
     __syncthreads();
     // the two vocab halves of each row, in order
     for (int rl = threadIdx.x; rl < HT; rl += HWAVES * 64) {
@@ -301,12 +334,13 @@ __global__ __launch_bounds__(HWAVES * 64) void head_tile_kernel(HeadTileArgs p, 
       if (row >= p.n) continue;
       const float ma = red_m[0][rl], mb = red_m[1][rl];
       const float m = fmaxf(ma, mb);
-      const float s = red_s[0][rl] * fast_exp2((ma - m) * kLog2e) +
-                      red_s[1][rl] * fast_exp2((mb - m) * kLog2e);
+      const float sum = red_s[0][rl] * fast_exp2((ma - m) * kLog2e) +
+                        red_s[1][rl] * fast_exp2((mb - m) * kLog2e);
       p.part_m[(size_t)vt * p.n + row] = m;
-      p.part_s[(size_t)vt * p.n + row] = s;
+      p.part_s[(size_t)vt * p.n + row] = sum;
     }
   } else {
+    const bool vfull = v0 + HT <= p.V;
     const bool vec = (p.V & 3) == 0;
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
@@ -323,9 +357,13 @@ __global__ __launch_bounds__(HWAVES * 64) void head_tile_kernel(HeadTileArgs p, 
           const int vq = vb + 32 * a + 8 * q + 4 * hi;
           float gv[4];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float e = fast_exp2(fmaf(acc[a][b][4 * q + j], kLog2e, -ll));
-            gv[j] = d * ((vq + j == tok ? 1.f : 0.f) - e);
+          for (int j = 0; j < 4; ++j)
+            gv[j] = -d * fast_exp2(fmaf(acc[a][b][4 * q + j], kLog2e, -ll));
+          const unsigned o = (unsigned)(tok - vq);
+          if (o < 4u) {  // the token's entry: d (1 - e)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              if (o == (unsigned)j) gv[j] += d;
           }
           if (vec && (vfull || vq < p.V)) {
             *reinterpret_cast<u32x2 *>(grow + vq) = pack4_bf16(gv[0], gv[1], gv[2], gv[3]);
@@ -339,25 +377,52 @@ __global__ __launch_bounds__(HWAVES * 64) void head_tile_kernel(HeadTileArgs p, 
   }
 }
 
-// lse and logp of scored row k from the per-tile (max, sum) pairs, in tile order.
+// One wave per scored row k: the target logit z[token] = H_pred[k] . W[token]
+// (fp32 dot product over d_model, 8 entries per lane and pass, then a xor
+// butterfly, so every lane holds the same sum), and lse from the per-tile
+// (max, sum) pairs: lane l combines tiles l, l + 64, ... in order, then a xor
+// butterfly of the pairs.  Both reductions have a fixed order.
 __global__ __launch_bounds__(256) void head_lse_combine_kernel(
-    const float *__restrict__ part_m, const float *__restrict__ part_s,
-    const float *__restrict__ ztok, const int32_t *__restrict__ scored_row,
+    const float *__restrict__ part_m, const float *__restrict__ part_s, const bf16 *__restrict__ hp,
+    const bf16 *__restrict__ w, const int32_t *__restrict__ scored_row,
     const int32_t *__restrict__ tokens, float *__restrict__ logp, float *__restrict__ lse, int n,
-    int V, int nvt) {
-  const int k = blockIdx.x * 256 + threadIdx.x;
+    int V, int dm, int nvt) {
+  const int lane = threadIdx.x & 63;
+  const int k = blockIdx.x * 4 + wave_id();
   if (k >= n) return;
-  float m = part_m[k], s = part_s[k];
-  for (int t = 1; t < nvt; ++t) {
+  const int tok = tokens[scored_row[k]];
+  const bool tok_ok = (unsigned)tok < (unsigned)V;
+  float zt = 0.f;
+  if (tok_ok) {
+    const bf16x8 *hr = reinterpret_cast<const bf16x8 *>(hp + (size_t)k * dm);
+    const bf16x8 *wr = reinterpret_cast<const bf16x8 *>(w + (size_t)tok * dm);
+    for (int c = lane; c < dm / 8; c += 64) {
+      const bf16x8 x = hr[c], y = wr[c];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) zt = fmaf((float)x[j], (float)y[j], zt);
+    }
+  }
+  float m = -INFINITY, s = 0.f;
+  for (int t = lane; t < nvt; t += 64) {
     const float m2 = part_m[(size_t)t * n + k], s2 = part_s[(size_t)t * n + k];
     const float mn = fmaxf(m, m2);
-    s = s * fast_exp2((m - mn) * kLog2e) + s2 * fast_exp2((m2 - mn) * kLog2e);
+    s = (m == -INFINITY ? 0.f : s * fast_exp2((m - mn) * kLog2e)) + s2 * fast_exp2((m2 - mn) * kLog2e);
     m = mn;
   }
-  const float l = m + __logf(s);
-  lse[k] = l;
-  const int tok = tokens[scored_row[k]];
-  logp[k] = (unsigned)tok < (unsigned)V ? ztok[k] - l : __int_as_float(0x7fc00000);  // NaN: bad id
+#pragma unroll
+  for (int x = 32; x >= 1; x >>= 1) {
+    zt += __shfl_xor(zt, x);
+    const float m2 = __shfl_xor(m, x), s2 = __shfl_xor(s, x);
+    const float mn = fmaxf(m, m2);
+    s = (m == -INFINITY ? 0.f : s * fast_exp2((m - mn) * kLog2e)) +
+        (m2 == -INFINITY ? 0.f : s2 * fast_exp2((m2 - mn) * kLog2e));
+    m = mn;
+  }
+  if (lane == 0) {
+    const float l = m + __logf(s);
+    lse[k] = l;
+    logp[k] = tok_ok ? zt - l : __int_as_float(0x7fc00000);  // NaN: bad id
+  }
 }
 
 HeadTileArgs tile_args(const void *hp, const void *w, int n, int V, int dm,
@@ -378,19 +443,19 @@ HeadTileArgs tile_args(const void *hp, const void *w, int n, int V, int dm,
 int head_vocab_tiles(int V) { return (V + HT - 1) / HT; }
 
 hipError_t launch_head_logprob(const void *hp, const void *w, const int32_t *scored_row,
-                               const int32_t *tokens, float *part_m, float *part_s, float *ztok,
-                               float *logp, float *lse, int n, int V, int dm, hipStream_t s) {
+                               const int32_t *tokens, float *part_m, float *part_s, float *logp,
+                               float *lse, int n, int V, int dm, hipStream_t s) {
   if (n == 0) return hipSuccess;
   const int nvt = head_vocab_tiles(V), nmt = (n + HT - 1) / HT;
   HeadTileArgs a = tile_args(hp, w, n, V, dm, scored_row, tokens);
   a.part_m = part_m;
   a.part_s = part_s;
-  a.ztok = ztok;
   hipLaunchKernelGGL(head_tile_kernel<0>, dim3(nvt * nmt), dim3(HWAVES * 64), 0, s, a, nvt, nmt);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(head_lse_combine_kernel, dim3((n + 255) / 256), dim3(256), 0, s, part_m,
-                     part_s, ztok, scored_row, tokens, logp, lse, n, V, nvt);
+  hipLaunchKernelGGL(head_lse_combine_kernel, dim3((n + 3) / 4), dim3(256), 0, s, part_m, part_s,
+                     (const bf16 *)hp, (const bf16 *)w, scored_row, tokens, logp, lse, n, V, dm,
+                     nvt);
   return hipGetLastError();
 }
 

@@ -81,10 +81,10 @@ hipError_t launch_gather_rows(const int32_t *pred, const void *hidden, void *out
 // number of 256-entry vocab tiles (rows of the per-tile max / sum arrays)
 int head_vocab_tiles(int V);
 // logp and lse of the n scored rows; part_m / part_s: [head_vocab_tiles(V), n]
-// floats, ztok: [n] floats of scratch
+// floats of scratch
 hipError_t launch_head_logprob(const void *hp, const void *w, const int32_t *scored_row,
-                               const int32_t *tokens, float *part_m, float *part_s, float *ztok,
-                               float *logp, float *lse, int n, int V, int dm, hipStream_t s);
+                               const int32_t *tokens, float *part_m, float *part_s, float *logp,
+                               float *lse, int n, int V, int dm, hipStream_t s);
 // G [n, V] bf16, the gradient of the loss with respect to the logits
 hipError_t launch_head_grad(const void *hp, const void *w, const int32_t *scored_row,
                             const int32_t *tokens, const float *lse, const float *dlogp, void *g,

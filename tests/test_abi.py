@@ -359,8 +359,7 @@ def test_head_sizes_and_validation():
     dhp = a256(hp) + n * dm * 4
     pm = a256(dhp) + nvt * n * 4
     ps = a256(pm) + nvt * n * 4
-    zt = a256(ps) + n * 4
-    want = a256(zt)
+    want = a256(ps)
     assert L.pg_logprob_workspace_size(ctypes.byref(desc), V, dm) == want
     assert L.pg_logprob_workspace_size(ctypes.byref(desc), 0, dm) == 0
     assert L.pg_logprob_workspace_size(ctypes.byref(desc), V, 12) == 0
