@@ -35,13 +35,11 @@
  *     workspaces are allocated and owned by the caller.
  *   - State the library itself holds, per process, until it ends (nothing is
  *     freed): (1) pg_pack's pinned, device-mapped host staging buffers, at
- *     most 64, reused once the upload kernel that reads them has run; (2) one
- *     rocBLAS handle per device, created by the first log-probability head
- *     call on it; (3) pg_attn_bwd_noalloc's device scratch array,
- *     PG_NOALLOC_SCRATCH_BYTES per device, placed by the HIP runtime when the
- *     library's code objects are loaded on that device; (4) the kernel timing
- *     table and its event pool (pg_kernel_timing); (5) the thread-local
- *     message of pg_last_error.  None of it carries results from one call to
+ *     most 64, reused once the upload kernel that reads them has run; (2)
+ *     pg_attn_bwd_noalloc's device scratch array, PG_NOALLOC_SCRATCH_BYTES per
+ *     device, placed by the HIP runtime when the library's code objects are
+ *     loaded on that device; (3) the kernel timing table and its event pool
+ *     (pg_kernel_timing); (4) the thread-local message of pg_last_error.  None of it carries results from one call to
  *     the next.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Kernels are
  *     enqueued on it; the call returns before they finish.
@@ -311,8 +309,9 @@ pg_status pg_rope(const pg_desc *d, pg_dtype t, void *x, int32_t num_heads, int3
  * kernels and reduced in place (forward: per-row max and sum of exponentials
  * per 256-entry vocab tile, and the target logit as one dot product;
  * backward: the gradient of the logits, stored as bf16), so they are never
- * written to memory; the
- * backward's two products dH = G weight and dW = G^T H run as rocBLAS GEMMs.
+ * written to memory; the backward's two products dH = G weight and dW = G^T H
+ * run on the same tile kernel, from G and G^T and transposed copies of weight
+ * and H.
  * hidden: bf16 [T, d_model] in packed order; weight: bf16 [vocab, d_model]
  * (under 4 GiB, as are the num_scored gathered hidden rows: larger heads
  * return PG_ERR_UNSUPPORTED); tokens: int32 [T] token id of every packed row
@@ -320,10 +319,13 @@ pg_status pg_rope(const pg_desc *d, pg_dtype t, void *x, int32_t num_heads, int3
  * d_model a multiple of 8.  Device buffers, 16-byte aligned, caller-owned. */
 
 /* Bytes of scratch pg_logprob_fwd / pg_logprob_bwd need: the gradient of the
- * logits (bf16 [num_scored, vocab]), the gathered predicting rows (bf16
- * [num_scored, d_model]) and their gradient (fp32), and the forward's
- * per-tile row max and sum (fp32 [ceil(vocab / 256), num_scored] each), each
- * 256-byte aligned.  0 if the arguments are invalid. */
+ * logits as bf16 [num_scored, V64] and [vocab, n64] (V64, n64: vocab and
+ * num_scored rounded up to multiples of 64), the gathered predicting rows
+ * (bf16 [num_scored, d_model]) and their transpose (bf16 [d_model, n64]), the
+ * transposed weight (bf16 [d_model, V64]), the predicting rows' gradient (fp32
+ * [num_scored, d_model]), and the forward's per-tile row max and sum (fp32
+ * [ceil(vocab / 256), num_scored] each), each 256-byte aligned.  0 if the
+ * arguments are invalid. */
 size_t pg_logprob_workspace_size(const pg_desc *d, int32_t vocab, int32_t d_model);
 
 /* logp [num_scored]: log-probability of each scored token; lse

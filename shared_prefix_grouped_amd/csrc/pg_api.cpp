@@ -9,7 +9,6 @@
 // token sees the whole prefix and its own response up to itself).
 
 #include <hip/hip_runtime.h>
-#include <rocblas/rocblas.h>
 
 #include <algorithm>
 #include <cmath>
@@ -564,67 +563,27 @@ pg_status rows_call(const pg_desc *d, bool pack, void *packed, void *pre, void *
 }
 
 // ---------------------------------------------------------------- log-prob head
-// One rocBLAS handle per device, created on first use; the stream is set and
-// the GEMMs are enqueued under the lock.  Atomics are disallowed, so the
-// GEMMs are deterministic.
-struct Blas {
-  std::mutex mu;
-  std::map<int, rocblas_handle> handles;
-};
-Blas &blas() {
-  static Blas b;
-  return b;
-}
-
-pg_status blas_status(rocblas_status st, const char *what) {
-  if (st == rocblas_status_success) return PG_OK;
-  return fail(PG_ERR_HIP, std::string(what) + ": " + rocblas_status_to_string(st));
-}
-
-// Row-major products with bf16 operands and fp32 results, as rocBLAS
-// column-major calls (a row-major [r x c] matrix is a column-major [c x r]).
-rocblas_status gemm_bf16(rocblas_handle h, rocblas_operation ta, rocblas_operation tb, int m, int n,
-                         int k, const void *A, int lda, const void *B, int ldb, float *D, int ldd) {
-  const float one = 1.f, zero = 0.f;
-  return rocblas_gemm_ex(h, ta, tb, m, n, k, &one, A, rocblas_datatype_bf16_r, lda, B,
-                         rocblas_datatype_bf16_r, ldb, &zero, D, rocblas_datatype_f32_r, ldd, D,
-                         rocblas_datatype_f32_r, ldd, rocblas_datatype_f32_r,
-                         rocblas_gemm_algo_standard, 0, 0);
-}
-
-pg_status get_blas(Blas &b, rocblas_handle *out) {  // b.mu held
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
-  auto it = b.handles.find(dev);
-  if (it == b.handles.end()) {
-    rocblas_handle h = nullptr;
-    pg_status st = blas_status(rocblas_create_handle(&h), "rocblas_create_handle");
-    if (st != PG_OK) return st;
-    if ((st = blas_status(rocblas_set_atomics_mode(h, rocblas_atomics_not_allowed),
-                          "rocblas_set_atomics_mode")) != PG_OK)
-      return st;
-    it = b.handles.emplace(dev, h).first;
-  }
-  *out = it->second;
-  return PG_OK;
-}
-
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// Workspace of the head: G [n, V] bf16 (the gradient of the loss with
-// respect to the logits), H_pred [n, dm] bf16, dH_pred [n, dm] fp32, and the
-// forward's per-vocab-tile row max and sum ([nvt, n] fp32 each).  The logits
+// Workspace of the head: the gradient of the loss with respect to the logits
+// as G [n, V64] and G^T [V, n64] bf16 (V64, n64: rounded up to multiples of
+// 64, so that rows start on 128-byte lines), H_pred [n, dm] and H_pred^T
+// [dm, n64] bf16, W^T [dm, V64] bf16, dH_pred [n, dm] fp32, and the forward's
+// per-vocab-tile row max and sum ([nvt, n] fp32 each).  The logits
 // themselves are never stored.
 struct HeadWs {
-  size_t g, hp, dhp, pm, ps, total;
+  size_t g, gt, hp, hpt, wt, dhp, pm, ps, total;
 };
 HeadWs head_ws(int64_t n, int64_t V, int64_t dm) {
   HeadWs w{};
   const size_t nvt = size_t(pg::head_vocab_tiles(int(V)));
+  const size_t n64 = size_t(pg::round64(int(n))), V64 = size_t(pg::round64(int(V)));
   w.g = 0;
-  w.hp = align256(w.g + size_t(n) * V * 2);
-  w.dhp = align256(w.hp + size_t(n) * dm * 2);
+  w.gt = align256(w.g + size_t(n) * V64 * 2);
+  w.hp = align256(w.gt + size_t(V) * n64 * 2);
+  w.hpt = align256(w.hp + size_t(n) * dm * 2);
+  w.wt = align256(w.hpt + size_t(dm) * n64 * 2);
+  w.dhp = align256(w.wt + size_t(dm) * V64 * 2);
   w.pm = align256(w.dhp + size_t(n) * dm * 4);
   w.ps = align256(w.pm + nvt * size_t(n) * 4);
   w.total = std::max<size_t>(256, align256(w.ps + nvt * size_t(n) * 4));
@@ -636,10 +595,15 @@ pg_status check_head(const pg_desc *d, int32_t vocab, int32_t d_model) {
   if (st != PG_OK) return st;
   if (vocab < 1 || d_model < 8 || d_model % 8)
     return fail(PG_ERR_INVALID_ARG, "vocab must be >= 1 and d_model a positive multiple of 8");
-  // the tile kernels address W and H_pred with 32-bit byte offsets
-  if (int64_t(vocab) * d_model * 2 >= (int64_t(1) << 32) ||
-      int64_t(d->num_scored) * d_model * 2 >= (int64_t(1) << 32))
-    return fail(PG_ERR_UNSUPPORTED, "weight and scored hidden rows must each be under 4 GiB");
+  // the tile kernels address each operand with 32-bit byte offsets: W,
+  // H_pred and the logit gradient G (and their transposes) must each be
+  // under 4 GiB
+  const int64_t n64 = (int64_t(d->num_scored) + 63) & ~int64_t(63);
+  const int64_t V64 = (int64_t(vocab) + 63) & ~int64_t(63);
+  const int64_t lim = int64_t(1) << 32;
+  if (V64 * d_model * 2 >= lim || n64 * d_model * 2 >= lim || n64 * V64 * 2 >= lim)
+    return fail(PG_ERR_UNSUPPORTED,
+                "weight, scored hidden rows and their logit gradient must each be under 4 GiB");
   if (d->num_scored < 0 || d->num_resp < 0)
     return fail(PG_ERR_INVALID_ARG, "descriptor is not one filled by pg_pack");
   if (d->num_scored > 0 && (!d->scored_row || !d->scored_pred || !d->scored_resp ||
@@ -647,10 +611,6 @@ pg_status check_head(const pg_desc *d, int32_t vocab, int32_t d_model) {
     return fail(PG_ERR_INVALID_ARG, "descriptor arrays are NULL");
   return PG_OK;
 }
-
-// The row-major backward products of the head, in rocBLAS terms:
-//   dH [n, dm] = G [n, V] W [V, dm]       -> (N, N): m = dm, n = n,  k = V
-//   dW [V, dm] = G^T H_pred               -> (N, T): m = dm, n = V,  k = n
 
 // ---------------------------------------------------------------- plan upload staging
 // pg_pack writes the plan into a pinned, device-mapped host buffer that the
@@ -1070,38 +1030,39 @@ pg_status pg_logprob_bwd(const pg_desc *d, const void *hidden, const void *weigh
     return fail(PG_ERR_WORKSPACE, "workspace too small: need " + std::to_string(w.total) +
                                       " bytes, got " + std::to_string(ws_bytes));
   char *ws = static_cast<char *>(workspace);
-  void *g = ws + w.g;
-  void *hp = ws + w.hp;
+  void *g = ws + w.g, *gt = ws + w.gt, *hp = ws + w.hp, *hpt = ws + w.hpt, *wt = ws + w.wt;
   float *dhp = reinterpret_cast<float *>(ws + w.dhp);
+  // contraction lengths (multiples of 8) and row strides (multiples of 64)
+  const int n8 = pg::round8(n), V8 = pg::round8(vocab);
+  const int n64 = pg::round64(n), V64 = pg::round64(vocab);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  Blas &b = blas();
-  std::lock_guard<std::mutex> lock(b.mu);
-  rocblas_handle h;
-  if ((st = get_blas(b, &h)) != PG_OK) return st;
-  if ((st = blas_status(rocblas_set_stream(h, s), "rocblas_set_stream")) != PG_OK) return st;
-  pg_status gst = PG_OK;
   hipError_t e = timed(PG_KERNEL_HEAD_BWD, s, [&] {
     hipError_t r = hipSuccess;
     if (n > 0) {
+      // operands of the two products, each contiguous along its contraction
       if ((r = pg::launch_gather_rows(d->scored_pred, hidden, hp, n, d_model, s)) != hipSuccess)
         return r;
-      if ((r = pg::launch_head_grad(hp, weight, d->scored_row, tokens, lse, dlogp, g, n, vocab,
+      if ((r = pg::launch_transpose_pad(hidden, d->scored_pred, n, d_model, hpt, n64, s)) !=
+          hipSuccess)
+        return r;
+      if ((r = pg::launch_transpose_pad(weight, nullptr, vocab, d_model, wt, V64, s)) !=
+          hipSuccess)
+        return r;
+      if ((r = pg::launch_head_grad(hp, weight, d->scored_row, tokens, lse, dlogp, g, gt, n, vocab,
                                     d_model, s)) != hipSuccess)
         return r;
-      if ((gst = blas_status(gemm_bf16(h, rocblas_operation_none, rocblas_operation_none, d_model,
-                                       n, vocab, weight, d_model, g, vocab, dhp, d_model),
-                             "dhidden GEMM")) != PG_OK)
-        return hipErrorUnknown;
+      // dH_pred [n, dm] = G W = G [n, V64] (W^T [dm, V64])^T over V8 entries
+      if ((r = pg::launch_nt_f32(g, wt, n, d_model, V8, V64, V64, dhp, d_model, s)) != hipSuccess)
+        return r;
     }
-    // dW = G^T H_pred (zeros when nothing is scored: k = 0, beta = 0)
-    if ((gst = blas_status(gemm_bf16(h, rocblas_operation_none, rocblas_operation_transpose,
-                                     d_model, vocab, n, hp, d_model, g, vocab, dweight, d_model),
-                           "dweight GEMM")) != PG_OK)
-      return hipErrorUnknown;
+    // dW [V, dm] = G^T H_pred = G^T [V, n64] (H_pred^T [dm, n64])^T over n8
+    // entries; zeros when nothing is scored (an empty contraction)
+    if ((r = pg::launch_nt_f32(gt, hpt, vocab, d_model, n8, n64, n64, dweight, d_model, s)) !=
+        hipSuccess)
+      return r;
     return pg::launch_scatter_rows(d->pred_start, d->pred_list, dhp, dhidden, d->total_rows,
                                    d_model, s);
   });
-  if (gst != PG_OK) return gst;
   return hip_status(e, "pg_logprob_bwd launch");
 }
 

@@ -73,9 +73,13 @@ hipError_t launch_upload(const void *src_dev, void *dst, size_t bytes, const voi
 hipError_t launch_rows(const Plan &p, bool pack, void *packed, void *pre, void *resp,
                        size_t row_bytes, hipStream_t s);
 
-// Log-probability head kernels.  The logits products run in this library's
-// MFMA tile kernels with the log-softmax in their epilogue; dH = G W and
-// dW = G^T H_pred are rocBLAS calls.
+// Log-probability head kernels: the logits products and the backward's two
+// products run on this library's MFMA tile kernel (pg_head_mfma.hip).
+inline int round8(int x) { return (x + 7) & ~7; }
+// row stride of the head's transposed and gradient operands: whole 128-byte
+// cache lines per row (a stride that is not a multiple of 128 bytes makes
+// every 128-byte copy chunk straddle two lines)
+inline int round64(int x) { return (x + 63) & ~63; }
 hipError_t launch_gather_rows(const int32_t *pred, const void *hidden, void *out, int n,
                               int d_model, hipStream_t s);
 // number of 256-entry vocab tiles (rows of the per-tile max / sum arrays)
@@ -85,10 +89,19 @@ int head_vocab_tiles(int V);
 hipError_t launch_head_logprob(const void *hp, const void *w, const int32_t *scored_row,
                                const int32_t *tokens, float *part_m, float *part_s, float *logp,
                                float *lse, int n, int V, int dm, hipStream_t s);
-// G [n, V] bf16, the gradient of the loss with respect to the logits
+// the gradient of the loss with respect to the logits, bf16, as G [n, round64(V)]
+// and G^T [V, round64(n)] (pad entries zero)
 hipError_t launch_head_grad(const void *hp, const void *w, const int32_t *scored_row,
                             const int32_t *tokens, const float *lse, const float *dlogp, void *g,
-                            int n, int V, int dm, hipStream_t s);
+                            void *gt, int n, int V, int dm, hipStream_t s);
+// c [M, ldc] fp32 = a [M, K] b [N, K]^T for bf16 a, b (row strides lda, ldb,
+// multiples of 8; K a multiple of 8; M lda 2 and N ldb 2 under 2^32)
+hipError_t launch_nt_f32(const void *a, const void *b, int M, int N, int K, int lda, int ldb,
+                         float *c, int ldc, hipStream_t s);
+// dst [C, ldd] bf16: dst[c][r] = src[rows ? rows[r] : r][c] for r < R, zero
+// for R <= r < ldd (ldd even, C a multiple of 8)
+hipError_t launch_transpose_pad(const void *src, const int32_t *rows, int R, int C, void *dst,
+                                int ldd, hipStream_t s);
 hipError_t launch_grpo_loss(const float *logp, const int32_t *scored_resp, const float *adv,
                             float *loss, float *dlogp, int n, int n_resp, hipStream_t s);
 hipError_t launch_scatter_rows(const int32_t *pred_start, const int32_t *pred_list,

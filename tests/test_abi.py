@@ -354,18 +354,23 @@ def test_head_sizes_and_validation():
     n, V, dm = 9, 1000, 64
     a256 = lambda x: -(-x // 256) * 256
     nvt = -(-V // 256)  # vocab tiles of the logits kernels
-    g = n * V * 2  # gradient of the logits, bf16; the logits are never stored
-    hp = a256(g) + n * dm * 2
-    dhp = a256(hp) + n * dm * 4
+    n64, V64 = -(-n // 64) * 64, -(-V // 64) * 64  # row strides: whole 128-byte lines
+    g = n * V64 * 2  # gradient of the logits, bf16; the logits are never stored
+    gt = a256(g) + V * n64 * 2  # and its transpose
+    hp = a256(gt) + n * dm * 2
+    hpt = a256(hp) + dm * n64 * 2
+    wt = a256(hpt) + dm * V64 * 2
+    dhp = a256(wt) + n * dm * 4
     pm = a256(dhp) + nvt * n * 4
     ps = a256(pm) + nvt * n * 4
     want = a256(ps)
     assert L.pg_logprob_workspace_size(ctypes.byref(desc), V, dm) == want
     assert L.pg_logprob_workspace_size(ctypes.byref(desc), 0, dm) == 0
     assert L.pg_logprob_workspace_size(ctypes.byref(desc), V, 12) == 0
-    # the logits kernels address W with 32-bit byte offsets: a 4 GiB head is refused
-    assert L.pg_logprob_workspace_size(ctypes.byref(desc), 1 << 20, 2048) == 0
-    assert L.pg_logprob_workspace_size(ctypes.byref(desc), (1 << 20) - 1, 2048) > 0
+    # the tile kernels address each operand with 32-bit byte offsets: a 4 GiB
+    # transposed weight (vocab rounded up to a multiple of 64) is refused
+    assert L.pg_logprob_workspace_size(ctypes.byref(desc), (1 << 20) - 63, 2048) == 0
+    assert L.pg_logprob_workspace_size(ctypes.byref(desc), (1 << 20) - 64, 2048) > 0
     p = ctypes.c_void_p(4096)
     assert L.pg_logprob_fwd(ctypes.byref(desc), p, p, V, dm, p, p, p, p, want - 1,
                             None) == pg.PG_ERR_WORKSPACE
