@@ -450,6 +450,19 @@ def decoder_bench(a, pg, torch) -> dict:
                          "unit": "TFLOP/s", "frac": round(t_min / (g_ms * 1e-3), 4), "traffic": None}}
 
 
+def traffic_probe(torch) -> None:
+    """One plain 1 GiB device copy, whose FETCH_SIZE / WRITE_SIZE counters
+    calibrate the kernels' HBM traffic in a counter run."""
+    n = (1 << 30) // 2
+    src = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"[bench] traffic probe: copied {n * 2} bytes")
+    del src, dst
+
+
 def grpo_head_bench(a, pg, torch) -> dict:
     """One step of the GRPO log-probability head on the head workload: pg_pack,
     pg_logprob_fwd, pg_grpo_loss, pg_logprob_bwd.  Credited 6 * N * V * d_model
@@ -489,6 +502,8 @@ def grpo_head_bench(a, pg, torch) -> dict:
     kt = pg.pg_kernel_times()
     pg.pg_kernel_timing(False)
     ms = start.elapsed_time(stop) / a.steps
+    if a.traffic_probe:
+        traffic_probe(torch)
     flops = 6.0 * n * w.vocab * w.d_model
     tf = flops / (ms * 1e-3) / 1e12
     (nb, tb), (nf, tfw) = kt["head_bwd"], kt["head_fwd"]
@@ -506,6 +521,14 @@ def grpo_head_bench(a, pg, torch) -> dict:
             "N(0,0.02^2) head, uniform token ids, N(0,1) rewards)",
             "config": {"workload": w.name, "scored_rows": n, "d_model": w.d_model, "vocab": w.vocab,
                        "packed_rows": rows_all, "repeated_prefix_rows": rows_rep},
+            "kernels_ms_per_launch": {"head_fwd": round(tfw / nf, 4), "head_bwd": round(bwd_ms, 4),
+                                      "grpo_loss": round(kt["grpo_loss"][1] / max(1, kt["grpo_loss"][0]), 4)},
+            # forward: one product (2 n V d_model); backward: the logits recomputed and
+            # the two gradient products (6 n V d_model), all executed
+            "kernel_rooflines": {
+                "head_fwd": {"avg_launch_ms": round(tfw / nf, 4),
+                             "tflops": round(2.0 * n * w.vocab * w.d_model / (tfw / nf * 1e-3) / 1e12, 1)},
+                "head_bwd": {"avg_launch_ms": round(bwd_ms, 4), "tflops": round(bwd_tf, 1)}},
             "roofline": {"bound": "mfma", "kernel": "head_bwd", "achieved": round(bwd_tf, 1),
                          "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(bwd_tf / PEAK_BF16_TFLOPS, 4),
                          "traffic": None}}
@@ -597,14 +620,7 @@ def main(argv=None) -> int:
         kernel_roof[name] = rec
 
     if a.traffic_probe:
-        n = (1 << 30) // 2
-        src = torch.ones(n, dtype=torch.bfloat16, device="cuda")
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        log(f"[bench] traffic probe: copied {n * 2} bytes")
-        del src, dst
+        traffic_probe(torch)
 
     speed = None
     base_ms = None
