@@ -34,7 +34,12 @@ value      effective TFLOP/s = 14 * d * Hq * pairs / step time, where pairs is
            layout (forward 4d, backward 10d per pair: the flash-attention
            convention; masked work and recomputation are not credited).
 roofline   the kernel with the largest share of the step, timed with HIP
-           events recorded by the library on the stream it launches on.
+           events recorded by the library on the stream it launches on
+           (bf16: matrix-core bound against the bf16 MFMA peak; float32:
+           vector-ALU bound against the fp32 FMA peak).
+speedup_vs_repeated_prefix  the same kernels on the repeated-prefix layout
+           (every [P; R_i] its own group): three alternating rounds of each
+           layout without per-kernel events, ratio of the median step times.
 cpu_baseline  the fp64 oracle (repeated-prefix baseline) on a bounded sample
            of the same workload, on this host's cores, credited with the same
            effective-FLOP formula for the rows it covered.
@@ -56,8 +61,11 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA
-PEAK_F32_TFLOPS = 157.3     # MI355X dense fp32
-PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector
+PEAK_F32_TFLOPS = 157.3     # MI355X dense fp32 (matrix cores; the decoder's fp32 products)
+# fp32 FMA on the vector units without packed (two-wide) instructions, which
+# this library's kernels are built without: 256 CUs x 4 SIMDs x 16 lanes x
+# 2 flop x 2.4 GHz
+PEAK_F32_VALU_TFLOPS = 78.6
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 METRIC = "grouped-attn fwd+bwd TFLOP/s & % MFMA peak; speedup vs repeated-prefix"
@@ -65,6 +73,8 @@ METRIC_FWD = "grouped-attn forward-only scoring TFLOP/s & % MFMA peak; speedup v
 
 # algorithmic flops per unmasked (query, key) pair and query head, per kernel
 KERNEL_FLOPS_PER_PAIR_D = {"fwd": 4, "bwd_dkdv": 8, "bwd_dq": 6}
+# float32: the backward is one launch doing the dK/dV and the dQ work (timed as bwd_dkdv)
+KERNEL_FLOPS_PER_PAIR_D_F32 = {"fwd": 4, "bwd_dkdv": 14}
 
 
 def log(*a):
@@ -103,7 +113,6 @@ def parse(argv=None):
 # kernel name in the library's timing table -> (profile key, sources it is built from)
 KERNEL_SOURCES = {
     "fwd": ("fwd_bf16_kernel", ["pg_fwd_bf16.hip"]),
-    "bwd_pre": ("bwd_pre_kernel", ["pg_bwd_bf16.hip"]),
     "bwd_dkdv": ("dkdv_bf16_kernel", ["pg_bwd_bf16.hip"]),
     "bwd_dq": ("dq_bf16_kernel", ["pg_bwd_bf16.hip"]),
 }
@@ -165,12 +174,13 @@ class Runner:
         pg.pg_attn_bwd(self.batch, self.q, self.k, self.v, self.o, self.lse, self.do, None,
                        dq=self.dq, dk=self.dk, dv=self.dv, workspace=self.ws)
 
-    def timed(self, steps, warmup):
+    def timed(self, steps, warmup, kernel_events=True):
         torch = self.torch
         for _ in range(warmup):
             self.step()
         torch.cuda.synchronize()
-        self.pg.pg_kernel_timing(True)
+        if kernel_events:
+            self.pg.pg_kernel_timing(True)
         start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
@@ -180,8 +190,10 @@ class Runner:
         stop.record()
         torch.cuda.synchronize()
         wall = (time.perf_counter() - t0) * 1e3
-        kernels = self.pg.pg_kernel_times()
-        self.pg.pg_kernel_timing(False)
+        kernels = None
+        if kernel_events:
+            kernels = self.pg.pg_kernel_times()
+            self.pg.pg_kernel_timing(False)
         return start.elapsed_time(stop) / steps, wall / steps, kernels
 
 
@@ -584,12 +596,15 @@ def main(argv=None) -> int:
     dom = max(per_launch, key=per_launch.get)
     T, hq, d = w.total_rows, w.num_q_heads, w.head_dim
     esz = 2 if w.dtype == "bf16" else 4
-    if dom in KERNEL_FLOPS_PER_PAIR_D:
-        alg = KERNEL_FLOPS_PER_PAIR_D[dom] * d * hq * pairs
+    # bf16 kernels run their products on the matrix cores; the float32 path
+    # is plain vector FMA
+    flops_table = KERNEL_FLOPS_PER_PAIR_D if w.dtype == "bf16" else KERNEL_FLOPS_PER_PAIR_D_F32
+    bound, peak_alu = ("mfma", PEAK_BF16_TFLOPS) if w.dtype == "bf16" else ("alu", PEAK_F32_VALU_TFLOPS)
+    if dom in flops_table:
+        alg = flops_table[dom] * d * hq * pairs
         achieved = alg / (per_launch[dom] * 1e-3) / 1e12
-        peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
-        roof = {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": peak,
-                "unit": "TFLOP/s", "frac": achieved / peak,
+        roof = {"kernel": dom, "bound": bound, "achieved": achieved, "peak": peak_alu,
+                "unit": "TFLOP/s", "frac": achieved / peak_alu,
                 "traffic": measured_traffic(w.name, dom),
                 "algorithmic_flop_per_launch": alg, "avg_launch_ms": per_launch[dom]}
     else:
@@ -603,15 +618,15 @@ def main(argv=None) -> int:
     # every kernel of the step against its own roofline: algorithmic MFMA rate
     # (attention kernels) and measured HBM bytes per launch from the committed
     # counter profile (null once the kernel's sources differ from the profiled ones)
-    peak_mfma = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     kernel_roof = {}
     for name, t_ms in per_launch.items():
         if not t_ms:
             continue
         rec = {"avg_launch_ms": round(t_ms, 4)}
-        if name in KERNEL_FLOPS_PER_PAIR_D:
-            tf = KERNEL_FLOPS_PER_PAIR_D[name] * d * hq * pairs / (t_ms * 1e-3) / 1e12
-            rec.update({"algorithmic_tflops": round(tf, 1), "frac_mfma_peak": round(tf / peak_mfma, 4)})
+        if name in flops_table:
+            tf = flops_table[name] * d * hq * pairs / (t_ms * 1e-3) / 1e12
+            rec.update({"algorithmic_tflops": round(tf, 3),
+                        ("frac_mfma_peak" if bound == "mfma" else "frac_alu_peak"): round(tf / peak_alu, 5)})
         hbm = measured_traffic(w.name, name)
         if hbm is not None:
             gbs = hbm / (t_ms * 1e-3) / 1e9
@@ -624,6 +639,7 @@ def main(argv=None) -> int:
 
     speed = None
     base_ms = None
+    speed_rounds = None
     if not a.no_baseline:
         # same kernels on the repeated-prefix layout: every [P; R_i] as its own group
         idx, bgroups, t = [], [], 0
@@ -637,11 +653,22 @@ def main(argv=None) -> int:
         idx_t = torch.from_numpy(np.concatenate(idx)).to("cuda")
         btens = [x.index_select(0, idx_t).contiguous() for x in tens]
         brun = Runner(pg, torch, bgroups, w, btens, forward_only=fwd_only)
-        bsteps = max(2, a.steps // 4)
-        base_ms, _, _ = brun.timed(bsteps, 1)
-        speed = base_ms / ms
-        log(f"[bench] repeated-prefix layout: {base_ms:.3f} ms/step over {bsteps} steps; "
-            f"speedup {speed:.2f}x (ideal {base_pairs / pairs:.2f}x)")
+        # Both layouts timed again, alternately, three rounds each without the
+        # per-kernel events; the speedup is the ratio of the medians.  A round is
+        # a quarter of the steps but at least ~20 ms of grouped steps: a step of
+        # tens of microseconds is host-bound and needs hundreds of steps, and the
+        # medians drop a round that caught a one-off host stall.
+        nst = min(2000, max(2, a.steps // 4, int(math.ceil(20.0 / ms))))
+        g_rounds, b_rounds = [], []
+        for _ in range(3):
+            g_rounds.append(run.timed(nst, min(10, nst), kernel_events=False)[0])
+            b_rounds.append(brun.timed(nst, min(10, nst), kernel_events=False)[0])
+        base_ms = float(np.median(b_rounds))
+        speed = base_ms / float(np.median(g_rounds))
+        speed_rounds = {"steps_per_round": nst, "grouped_ms": [round(x, 4) for x in g_rounds],
+                        "repeated_prefix_ms": [round(x, 4) for x in b_rounds]}
+        log(f"[bench] repeated-prefix layout: {base_ms:.3f} ms/step (median of 3 rounds of {nst} steps, "
+            f"grouped {np.median(g_rounds):.3f}); speedup {speed:.2f}x (ideal {base_pairs / pairs:.2f}x)")
         del brun, btens
 
     cpu = None
@@ -661,9 +688,11 @@ def main(argv=None) -> int:
                    "effective_flop_per_step": eff_flops,
                    "step": ("pg_pack + pg_attn_fwd (no logsumexp)" if fwd_only
                             else "pg_pack + pg_attn_fwd + pg_attn_bwd")},
-        "pct_mfma_peak": round(100.0 * value / (PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS), 2),
+        "pct_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2) if w.dtype == "bf16" else None,
+        "pct_alu_peak": None if w.dtype == "bf16" else round(100.0 * value / PEAK_F32_VALU_TFLOPS, 4),
         "speedup_vs_repeated_prefix": None if speed is None else round(speed, 3),
         "repeated_prefix_ms_per_step": None if base_ms is None else round(base_ms, 4),
+        "speedup_rounds": speed_rounds,
         "ideal_speedup_pairs": round(base_pairs / pairs, 3),
         "kernels_ms_per_launch": {n: round(v, 4) for n, v in per_launch.items() if v},
         "host_wall_ms_per_step": round(wall_ms, 4),

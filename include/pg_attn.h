@@ -240,10 +240,12 @@ pg_status pg_unpack_rows(const pg_desc *d, const void *packed_rows, void *prefix
 pg_status pg_attn_fwd(const pg_desc *d, pg_dtype t, float softmax_scale, const void *q,
                       const void *k, const void *v, void *o, float *lse, void *stream);
 
-/* Bytes of scratch pg_attn_bwd needs: two float [Hq, T] arrays, rowsum(dO * O)
- * and the logsumexp in base 2, each 16-byte aligned, and for PG_BF16 the
+/* Bytes of scratch pg_attn_bwd needs.  PG_BF16: two float [Hq, T] arrays,
+ * rowsum(dO * O) and the logsumexp in base 2, each 16-byte aligned, and the
  * partial dK/dV sums of the cut key tiles, float
- * [num_kv_parts][num_kv_heads][2][PG_TILE_KV][head_dim]. */
+ * [num_kv_parts][num_kv_heads][2][PG_TILE_KV][head_dim].  PG_F32: 16 (its
+ * one backward launch computes both row statistics where it uses them and
+ * sums its partial results on chip). */
 size_t pg_attn_bwd_workspace_size(const pg_desc *d, pg_dtype t);
 
 /* Backward: gradients of sum(O * dO) with respect to Q, K, V, recomputing the
@@ -358,7 +360,11 @@ pg_status pg_logprob_bwd(const pg_desc *d, const void *hidden, const void *weigh
  * and returns the number of launches and their total duration in milliseconds
  * for one kernel id (PG_KERNEL_*); it fails with PG_ERR_INVALID_ARG for an
  * unknown id.  pg_kernel_name returns the kernel's name, or NULL.  Not
- * thread-safe with respect to concurrent enabling/reading. */
+ * thread-safe with respect to concurrent enabling/reading.  The PG_F32
+ * backward is one launch doing both the dK/dV and the dQ work, counted under
+ * PG_KERNEL_BWD_DKDV; PG_KERNEL_BWD_PRE counts nothing (both backward paths
+ * compute their row statistics inside their own kernels; the id keeps the
+ * numbering). */
 #define PG_KERNEL_FWD 0
 #define PG_KERNEL_BWD_PRE 1
 #define PG_KERNEL_BWD_DKDV 2

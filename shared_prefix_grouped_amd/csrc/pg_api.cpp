@@ -762,15 +762,10 @@ pg_status attn_bwd(const pg_desc *d, pg_dtype t, float softmax_scale, const void
       });
     return hip_status(e, "pg_attn_bwd launch");
   }
-  e = run(PG_KERNEL_BWD_PRE, [&] { return pg::launch_bwd_pre(p, t, o, dout, lse, delta, lse2, s); });
-  if (e != hipSuccess) return hip_status(e, "pg_attn_bwd preprocess launch");
+  // float32: one launch (dK/dV and dQ workgroups), timed as the dK/dV kernel
   e = run(PG_KERNEL_BWD_DKDV, [&] {
-    return pg::launch_bwd_dkdv_f32(p, scale, q, k, v, lse2, delta, dout, dk, dv, s);
+    return pg::launch_bwd_f32(p, scale, q, k, v, o, lse, dout, dq, dk, dv, s);
   });
-  if (e == hipSuccess)
-    e = run(PG_KERNEL_BWD_DQ, [&] {
-      return pg::launch_bwd_dq_f32(p, scale, q, k, v, lse2, delta, dout, dq, s);
-    });
   return hip_status(e, "pg_attn_bwd launch");
 }
 
@@ -890,13 +885,14 @@ pg_status pg_attn_fwd(const pg_desc *d, pg_dtype t, float softmax_scale, const v
 
 size_t pg_attn_bwd_workspace_size(const pg_desc *d, pg_dtype t) {
   if (check_desc(d) != PG_OK) return 0;
-  // delta and the base-2 logsumexp, float [Hq, T] each; for bf16 also the
-  // float dK/dV partial sums of the split key tiles
+  // float32: the backward computes delta and the logsumexp where it uses them
+  // and keeps its partial sums on chip
+  if (t != PG_BF16) return 16;
+  // bf16: delta and the base-2 logsumexp, float [Hq, T] each, and the float
+  // dK/dV partial sums of the split key tiles
   const size_t rows = align16(size_t(d->num_q_heads) * size_t(d->total_rows) * 4);
-  size_t parts = 0;
-  if (t == PG_BF16)
-    parts = size_t(d->num_kv_parts) * size_t(d->num_kv_heads) * 2 * PG_TILE_KV *
-            size_t(d->head_dim) * 4;
+  const size_t parts = size_t(d->num_kv_parts) * size_t(d->num_kv_heads) * 2 * PG_TILE_KV *
+                       size_t(d->head_dim) * 4;
   return std::max<size_t>(16, 2 * rows + parts);
 }
 

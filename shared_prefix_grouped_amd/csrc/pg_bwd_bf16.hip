@@ -27,36 +27,6 @@
 namespace pg {
 namespace {
 
-// ---------------------------------------------------------------- preprocess
-// delta[h][t] = sum_d dO[t][h][d] * O[t][h][d], in float, and
-// lse2[h][t] = LSE[h][t] * log2(e) (the backward kernels work in base 2).
-template <typename Tin, int D>
-__global__ __launch_bounds__(256) void bwd_pre_kernel(const Tin *__restrict__ O,
-                                                      const Tin *__restrict__ dO,
-                                                      const float *__restrict__ lse,
-                                                      float *__restrict__ delta,
-                                                      float *__restrict__ lse2, int T, int Hq) {
-  constexpr int TPR = D / 8;            // threads per (row, head), 8 elements each
-  constexpr int RPB = 256 / TPR;        // (row, head) pairs per block
-  const int tid = threadIdx.x;
-  const long long rh = (long long)blockIdx.x * RPB + tid / TPR;
-  const int part = tid % TPR;
-  float acc = 0.f;
-  if (rh < (long long)T * Hq) {
-    const Tin *o = O + rh * D + part * 8;
-    const Tin *g = dO + rh * D + part * 8;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc += (float)o[j] * (float)g[j];
-  }
-#pragma unroll
-  for (int w = TPR / 2; w >= 1; w >>= 1) acc += __shfl_xor(acc, w);
-  if (rh < (long long)T * Hq && part == 0) {
-    const int t = (int)(rh / Hq), h = (int)(rh % Hq);
-    delta[(size_t)h * T + t] = acc;
-    lse2[(size_t)h * T + t] = lse[(size_t)h * T + t] * kLog2e;
-  }
-}
-
 // ---------------------------------------------------------------- dK, dV
 // A workgroup owns 128 key rows of one kv head, as 4 groups of 32 keys, and
 // runs 8 waves, two per key group.  Wave A holds the group's K and V rows and
@@ -670,30 +640,6 @@ __global__ __launch_bounds__(256, 2) void dq_bf16_kernel(
 }
 
 }  // namespace
-
-hipError_t launch_bwd_pre(const Plan &p, pg_dtype t, const void *o, const void *dout,
-                          const float *lse, float *delta, float *lse2, hipStream_t s) {
-  const long long rows = (long long)p.T * p.Hq;
-  if (rows == 0) return hipSuccess;
-  const int rpb = 256 / (p.D / 8);
-  const dim3 grid((unsigned)((rows + rpb - 1) / rpb)), block(256);
-  if (t == PG_BF16) {
-    if (p.D == 128)
-      hipLaunchKernelGGL((bwd_pre_kernel<__bf16, 128>), grid, block, 0, s, (const __bf16 *)o,
-                         (const __bf16 *)dout, lse, delta, lse2, p.T, p.Hq);
-    else
-      hipLaunchKernelGGL((bwd_pre_kernel<__bf16, 64>), grid, block, 0, s, (const __bf16 *)o,
-                         (const __bf16 *)dout, lse, delta, lse2, p.T, p.Hq);
-  } else {
-    if (p.D == 128)
-      hipLaunchKernelGGL((bwd_pre_kernel<float, 128>), grid, block, 0, s, (const float *)o,
-                         (const float *)dout, lse, delta, lse2, p.T, p.Hq);
-    else
-      hipLaunchKernelGGL((bwd_pre_kernel<float, 64>), grid, block, 0, s, (const float *)o,
-                         (const float *)dout, lse, delta, lse2, p.T, p.Hq);
-  }
-  return hipGetLastError();
-}
 
 hipError_t launch_bwd_dkdv_bf16(const Plan &p, float scale, const void *q, const void *k,
                                 const void *v, const float *lse, const float *delta,

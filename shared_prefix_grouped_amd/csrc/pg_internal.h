@@ -38,14 +38,9 @@ hipError_t launch_fwd_bf16(const Plan &p, float scale, const void *q, const void
 hipError_t launch_fwd_f32(const Plan &p, float scale, const void *q, const void *k,
                           const void *v, void *o, float *lse, hipStream_t s);
 
-// Backward preprocess (float32 path): delta[h][t] = sum_d dO[t][h][d] *
-// O[t][h][d] (float) and lse2 = LSE * log2(e).  The bf16 dQ kernel computes
-// both itself for the rows it owns and stores them for the bf16 dK/dV kernel.
-hipError_t launch_bwd_pre(const Plan &p, pg_dtype t, const void *o, const void *dout,
-                          const float *lse, float *delta, float *lse2, hipStream_t s);
-// dK, dV (key-stationary) and dQ (query-stationary); no atomics.  `lse`
-// passed to dK/dV is the base-2 logsumexp (written by the preprocess or, for
-// bf16, by the dQ kernel, which takes the forward's natural-log LSE).  The
+// bf16 dK, dV (key-stationary) and dQ (query-stationary); no atomics.  `lse`
+// passed to dK/dV is the base-2 logsumexp written, with delta, by the dQ
+// kernel, which takes the forward's natural-log LSE.  The
 // bf16 dK/dV launch walks the plan's kv_items; `partial` holds n_kv_parts
 // float slots of [Hkv][2][PG_TILE_KV][D] for the pieces of split key tiles.
 hipError_t launch_bwd_dkdv_bf16(const Plan &p, float scale, const void *q, const void *k,
@@ -55,12 +50,12 @@ hipError_t launch_bwd_dkdv_bf16(const Plan &p, float scale, const void *q, const
 hipError_t launch_bwd_dq_bf16(const Plan &p, float scale, const void *q, const void *k,
                               const void *v, const void *o, const float *lse, float *lse2,
                               float *delta, const void *dout, void *dq, hipStream_t s);
-hipError_t launch_bwd_dkdv_f32(const Plan &p, float scale, const void *q, const void *k,
-                               const void *v, const float *lse, const float *delta,
-                               const void *dout, void *dk, void *dv, hipStream_t s);
-hipError_t launch_bwd_dq_f32(const Plan &p, float scale, const void *q, const void *k,
-                             const void *v, const float *lse, const float *delta,
-                             const void *dout, void *dq, hipStream_t s);
+// Float32 backward: one launch of dK/dV and dQ workgroups, which compute
+// delta and the base-2 logsumexp themselves from O, dO and the forward's
+// natural-log `lse`.
+hipError_t launch_bwd_f32(const Plan &p, float scale, const void *q, const void *k,
+                          const void *v, const void *o, const float *lse, const void *dout,
+                          void *dq, void *dk, void *dv, hipStream_t s);
 
 // Plan upload: `bytes` (a multiple of 16) from src_dev to dst and npos int32
 // position ids from pos_src_dev to pos_dst, where the sources are device

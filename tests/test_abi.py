@@ -279,7 +279,7 @@ def test_fwd_bwd_validate_before_launch():
     rows = -(-desc.num_q_heads * desc.total_rows * 4 // 16) * 16
     assert ws == max(16, 2 * rows + desc.num_kv_parts * desc.num_kv_heads * 2 * pg.PG_TILE_KV
                      * desc.head_dim * 4)
-    assert L.pg_attn_bwd_workspace_size(ctypes.byref(desc), pg.PG_F32) == max(16, 2 * rows)
+    assert L.pg_attn_bwd_workspace_size(ctypes.byref(desc), pg.PG_F32) == 16
     cut, _cbuf = _host_desc(((40, [97] * 24),), 8, 2, 128)  # one cut prefix tile
     assert cut.num_kv_parts >= 2
     rows_c = -(-8 * cut.total_rows * 4 // 16) * 16
