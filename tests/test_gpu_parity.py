@@ -79,6 +79,9 @@ SMALL = [
     ("short_prefix_g24", [(40, [97] * 24)], 8, 2, 128),
     ("short_prefix_2groups_d64", [(150, [61] * 20 + [3, 200]), (7, [33] * 12)], 4, 2, 64),
     ("short_prefix_mha", [(130, [50] * 40)], 2, 2, 128),
+    # several plan tiles per group, long walks over many staged chunks (float32
+    # path: 32-row chunks, 8-row sub-tiles), a second group after a long one
+    ("multi_tile_two_groups", [(1000, [333, 12, 700]), (64, [500])], 8, 2, 128),
 ]
 
 
