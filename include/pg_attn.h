@@ -107,7 +107,7 @@ typedef struct {
  *   row_lo[T]    first key row of the row's own segment: the group's first
  *                row for a prefix row, the response's first row for a
  *                response row.  A query row q sees key rows
- *                [group start, prefix end) and [row_lo[q], q].
+ *                [group start, min(prefix end, q + 1)) and [row_lo[q], q].
  *   row_hi[T]    one past the last query row that sees key row k: the group's
  *                end for a prefix row, the response's end for a response row.
  *                Key row k is seen by exactly the query rows [k, row_hi[k]).
