@@ -143,12 +143,16 @@ def _check(status: int) -> None:
 
 
 def _groups_struct(groups, hq, hkv, d):
-    prefix = np.ascontiguousarray([int(p) for p, _ in groups], dtype=np.int32)
-    nresp = np.ascontiguousarray([len(rs) for _, rs in groups], dtype=np.int32)
-    rlen = np.ascontiguousarray([int(r) for _, rs in groups for r in rs], dtype=np.int32)
-    keep = (prefix, nresp, rlen)  # arrays must outlive the struct's use
-    ptr = lambda a: a.ctypes.data_as(_i32p) if a.size else _i32p()
-    g = PgGroups(len(prefix), ptr(prefix), ptr(nresp), ptr(rlen), int(hq), int(hkv), int(d))
+    prefix = [int(p) for p, _ in groups]
+    nresp = [len(rs) for _, rs in groups]
+    rlen = [int(r) for _, rs in groups for r in rs]
+    # one int32 array holding the three lists (values outside int32 raise);
+    # it must outlive the struct's use
+    keep = np.array(prefix + nresp + rlen, dtype=np.int32)
+    base = keep.ctypes.data
+    ng, nr = len(prefix), len(rlen)
+    ptr = lambda off, n: ctypes.cast(base + 4 * off, _i32p) if n else _i32p()
+    g = PgGroups(ng, ptr(0, ng), ptr(ng, ng), ptr(2 * ng, nr), int(hq), int(hkv), int(d))
     return g, keep
 
 
@@ -158,8 +162,17 @@ def _torch():
 
 
 def _stream_ptr(device) -> ctypes.c_void_p:
+    """The current stream of `device` (what torch would launch on) as a raw handle.
+
+    torch's own raw-stream query when it has one: the public current_stream()
+    builds a Stream object per call, which costs more than the kernel launch
+    for small batches."""
     torch = _torch()
-    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if raw is None:
+        return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+    idx = device.index if device.index is not None else torch.cuda.current_device()
+    return ctypes.c_void_p(raw(idx))
 
 
 @dataclass
