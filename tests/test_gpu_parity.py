@@ -82,6 +82,8 @@ SMALL = [
     # several plan tiles per group, long walks over many staged chunks (float32
     # path: 32-row chunks, 8-row sub-tiles), a second group after a long one
     ("multi_tile_two_groups", [(1000, [333, 12, 700]), (64, [500])], 8, 2, 128),
+    # 16 query heads on one kv head: every dK/dV walk sums 16 heads
+    ("gqa16_d64", [(190, [70, 5, 130])], 16, 1, 64),
 ]
 
 
