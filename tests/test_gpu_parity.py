@@ -94,6 +94,16 @@ def test_small_layouts(name, groups, hq, hkv, d, dtype):
     _full_check(w)
 
 
+def test_fp32_at_headline_shape_kv_head0():
+    """The float32 path at the GQA 32/8, G=16, P=8192 shape (T=15139): walks of
+    hundreds of staged chunks and thousands of workgroups; every row of kv head
+    0 (its 4 query heads) against the oracle, to the float32 tolerance."""
+    hw = attention_workloads()["bf16_gqa_g16_p8192"]
+    w = scaled_down("fp32_gqa_g16_p8192", _groups_of(hw), "f32", hw.num_q_heads,
+                    hw.num_kv_heads, hw.head_dim, seed=11)
+    _full_check(w, kv_heads=[0])
+
+
 def test_bf16_g8_p4096_full_size_kv_subset():
     """Full-size 32-head workload on the GPU; oracle on kv heads 0 and 31, every row."""
     _full_check(attention_workloads()["bf16_g8_p4096"], kv_heads=[0, 31])
