@@ -104,6 +104,25 @@ def test_fp32_at_headline_shape_kv_head0():
     _full_check(w, kv_heads=[0])
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_sharp_softmax_custom_scale(dtype):
+    """softmax_scale = 8/sqrt(d) instead of 1/sqrt(d): scores of standard
+    deviation about 8, so a row's running maximum keeps jumping by more than
+    the forward's lazy-rescale threshold and probabilities span many orders of
+    magnitude; the scale reaches every kernel through the C ABI."""
+    groups = [(300, [130, 7, 64])]
+    w = scaled_down("sharp_softmax", groups, dtype, 4, 2, 128, seed=21)
+    arrs = draw_attention_inputs(w)
+    scale = 8.0 / math.sqrt(128)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    out = run_gpu(groups, 4, 2, 128, arrs, tdt, scale=scale)
+    ref = repeated_prefix_attention(groups, arrs["q"], arrs["k"], arrs["v"], arrs["do"], scale=scale)
+    gpu = {"o": to_np(out["o"]), "lse": to_np(out["lse"]), "dq": to_np(out["dq"]),
+           "dk": to_np(out["dk"]), "dv": to_np(out["dv"])}
+    msgs = compare(gpu, ref, dtype, prefix_mask=segment_rows(groups))
+    _say(f"[parity] sharp softmax ({dtype}, scale {scale:.3f}): " + "; ".join(msgs))
+
+
 def test_bf16_g8_p4096_full_size_kv_subset():
     """Full-size 32-head workload on the GPU; oracle on kv heads 0 and 31, every row."""
     _full_check(attention_workloads()["bf16_g8_p4096"], kv_heads=[0, 31])
