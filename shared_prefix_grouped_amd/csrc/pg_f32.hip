@@ -105,8 +105,8 @@ __device__ __forceinline__ void loadn(float (&a)[N], const float *__restrict__ p
   }
 }
 
-// Staging of one chunk: 16-byte piece n of thread t is float4 i = t + 256 n of
-// the chunk's [kChunk][D] rows.
+// Staging of one chunk: 16-byte piece n of thread t is float4
+// i = t + kF32Threads * n of the chunk's [kChunk][D] rows.
 template <int D>
 struct ChunkPiece {
   int row, col;  // row within the chunk, first column
@@ -115,7 +115,7 @@ struct ChunkPiece {
     row = i / (D / 4);
     col = (i % (D / 4)) * 4;
   }
-  // offset of the piece in a staged tensor ([part][row][16] layout)
+  // offset of the piece in a staged tensor ([part][row][SL] layout)
   __device__ __forceinline__ int lds() const {
     constexpr int SL = F32Split<D>::SL;
     return (col / SL) * F32Split<D>::PART + row * SL + col % SL;
