@@ -418,6 +418,8 @@ def _head_args(batch, hidden, weight, tokens):
         raise PgError(PG_ERR_INVALID_ARG, "weight must be contiguous [vocab, d_model]")
     if tokens.dtype != torch.int32 or tokens.shape != (d.total_rows,) or not tokens.is_contiguous():
         raise PgError(PG_ERR_INVALID_ARG, "tokens must be contiguous int32 [T]")
+    if weight.device != hidden.device or tokens.device != hidden.device:
+        raise PgError(PG_ERR_INVALID_ARG, "hidden, weight and tokens must be on one device")
     return d, int(weight.shape[0]), int(hidden.shape[1])
 
 
@@ -446,10 +448,22 @@ def pg_logprob_fwd(batch: PackedBatch, hidden, weight, tokens, workspace=None):
     return logp[:n], lse[:n]
 
 
+def _f32_vector(name, x, n, device):
+    """Refuse (before any launch) a float32 vector input shorter than n entries,
+    strided, or on another device: the kernels read n entries."""
+    torch = _torch()
+    if x.dtype != torch.float32 or x.dim() != 1 or x.shape[0] < n or not x.is_contiguous():
+        raise PgError(PG_ERR_INVALID_ARG, f"{name} must be a contiguous float32 vector of {n} entries")
+    if x.device != device:
+        raise PgError(PG_ERR_INVALID_ARG, f"{name} is on {x.device}, expected {device}")
+
+
 def pg_grpo_loss(batch: PackedBatch, logp, advantages):
     """(loss [1], dlogp [num_scored]) of -mean_i(A_i * sum of response i's logp)."""
     torch = _torch()
     d = batch.desc
+    _f32_vector("advantages", advantages, d.num_resp, advantages.device)
+    _f32_vector("logp", logp, d.num_scored, advantages.device)
     loss = torch.empty(1, dtype=torch.float32, device=advantages.device)
     dlogp = torch.empty(max(d.num_scored, 1), dtype=torch.float32, device=advantages.device)
     _check(lib().pg_grpo_loss(ctypes.byref(d), _vp(logp), _vp(advantages), _vp(loss), _vp(dlogp),
@@ -461,6 +475,8 @@ def pg_logprob_bwd(batch: PackedBatch, hidden, weight, tokens, lse, dlogp, works
     """(dhidden fp32 [T, d_model], dweight fp32 [vocab, d_model])."""
     torch = _torch()
     d, vocab, d_model = _head_args(batch, hidden, weight, tokens)
+    _f32_vector("lse", lse, d.num_scored, hidden.device)
+    _f32_vector("dlogp", dlogp, d.num_scored, hidden.device)
     dh = torch.empty((max(d.total_rows, 1), d_model), dtype=torch.float32, device=hidden.device)
     dw = torch.empty((vocab, d_model), dtype=torch.float32, device=hidden.device)
     ws, need = _head_workspace(d, vocab, d_model, hidden.device, workspace)

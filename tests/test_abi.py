@@ -437,3 +437,31 @@ def test_binding_checks_backward_outputs_before_launch():
     with pytest.raises(pg.PgError) as e:
         pg.pg_attn_bwd(batch, q, kv, kv, q, lse, q, workspace=torch.zeros(4, dtype=torch.uint8))
     assert e.value.status == pg.PG_ERR_WORKSPACE
+
+
+def test_binding_checks_head_vectors_before_launch():
+    """lse / dlogp of the head backward and logp / advantages of the loss that
+    are short, of the wrong type or strided are refused by the binding before
+    the library is called (CPU tensors: a wrong one never reaches a kernel)."""
+    import torch
+    desc, _buf = _host_desc(((5, [3, 2]),), 2, 1, 64)
+    batch = pg.PackedBatch(desc, None, None, ((5, (3, 2)),))
+    n, T, dm, V = desc.num_scored, desc.total_rows, 16, 11
+    assert n > 0
+    h = torch.zeros((T, dm), dtype=torch.bfloat16)
+    W = torch.zeros((V, dm), dtype=torch.bfloat16)
+    tok = torch.zeros(T, dtype=torch.int32)
+    good = torch.zeros(n, dtype=torch.float32)
+    for bad in (torch.zeros(n - 1), torch.zeros(n, dtype=torch.float64), torch.zeros(2 * n)[::2]):
+        for which in ("lse", "dlogp"):
+            args = {"lse": good, "dlogp": good}
+            args[which] = bad
+            with pytest.raises(pg.PgError) as e:
+                pg.pg_logprob_bwd(batch, h, W, tok, args["lse"], args["dlogp"])
+            assert which in str(e.value)
+    with pytest.raises(pg.PgError) as e:
+        pg.pg_grpo_loss(batch, good, torch.zeros(desc.num_resp - 1))
+    assert "advantages" in str(e.value)
+    with pytest.raises(pg.PgError) as e:
+        pg.pg_grpo_loss(batch, torch.zeros(n - 1), torch.zeros(desc.num_resp))
+    assert "logp" in str(e.value)
