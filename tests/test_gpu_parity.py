@@ -123,6 +123,29 @@ def test_sharp_softmax_custom_scale(dtype):
     _say(f"[parity] sharp softmax ({dtype}, scale {scale:.3f}): " + "; ".join(msgs))
 
 
+def _random_layout(seed):
+    """A seeded random varlen batch: 1-3 groups, prefixes 0-400 rows, 1-12
+    responses of 0-200 rows each, a random head configuration and d."""
+    rng = np.random.default_rng(1000 + seed)
+    groups = []
+    for _ in range(int(rng.integers(1, 4))):
+        P = int(rng.integers(0, 401))
+        rs = [int(r) for r in rng.integers(0, 201, size=int(rng.integers(1, 13)))]
+        if P + sum(rs) == 0:
+            rs[0] = 1
+        groups.append((P, rs))
+    hq, hkv = [(2, 1), (4, 2), (8, 2), (4, 4), (16, 2)][int(rng.integers(0, 5))]
+    d = (64, 128)[int(rng.integers(0, 2))]
+    return groups, hq, hkv, d
+
+
+@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_random_layouts(seed, dtype):
+    groups, hq, hkv, d = _random_layout(seed)
+    _full_check(scaled_down(f"random_{seed}", groups, dtype, hq, hkv, d, seed=seed))
+
+
 def test_bf16_g8_p4096_full_size_kv_subset():
     """Full-size 32-head workload on the GPU; oracle on kv heads 0 and 31, every row."""
     _full_check(attention_workloads()["bf16_g8_p4096"], kv_heads=[0, 31])
