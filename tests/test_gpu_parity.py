@@ -123,6 +123,25 @@ def test_sharp_softmax_custom_scale(dtype):
     _say(f"[parity] sharp softmax ({dtype}, scale {scale:.3f}): " + "; ".join(msgs))
 
 
+# Head configurations beyond the ones above: kv head counts that are multiples
+# of 8 take the XCD-aware block-to-work maps (one or two kv heads per XCD, 1-3
+# query heads per kv head); the others the plain maps, with odd GQA ratios.
+HEADS = [
+    ("xcd_rep3", [(150, [90, 7, 61])], 24, 8, 128),
+    ("xcd_two_kv_per_xcd", [(97, [64, 130]), (33, [5])], 32, 16, 64),
+    ("xcd_mha16", [(70, [40, 41])], 16, 16, 128),
+    ("rep3_plain", [(200, [33, 120, 1])], 12, 4, 128),
+    ("rep5_plain", [(66, [100, 20])], 10, 2, 64),
+    ("odd_kv3", [(129, [31, 64])], 6, 3, 128),
+]
+
+
+@pytest.mark.parametrize("name,groups,hq,hkv,d", HEADS, ids=[s[0] for s in HEADS])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_head_configurations(name, groups, hq, hkv, d, dtype):
+    _full_check(scaled_down(name, groups, dtype, hq, hkv, d, seed=zlib.crc32(name.encode()) % 1000))
+
+
 def _random_layout(seed):
     """A seeded random varlen batch: 1-3 groups, prefixes 0-400 rows, 1-12
     responses of 0-200 rows each, a random head configuration and d."""
