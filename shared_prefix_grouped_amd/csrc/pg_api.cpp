@@ -458,6 +458,9 @@ struct Timing {
   std::vector<hipEvent_t> pool;
   int64_t launches[PG_KERNEL_COUNT] = {};
   double total_ms[PG_KERNEL_COUNT] = {};
+  // first error met by a non-waiting drain inside a launch, reported by the
+  // next timing query (the launch that triggered the drain is not at fault)
+  hipError_t deferred = hipSuccess;
 };
 
 Timing &timing() {
@@ -518,7 +521,10 @@ hipError_t timed(int id, hipStream_t s, F &&launch) {
     return e;
   }
   t.pending.push_back({id, a, b});
-  if (t.pending.size() > 4096) drain(t, false);
+  if (t.pending.size() > 4096) {
+    const hipError_t q = drain(t, false);
+    if (q != hipSuccess && t.deferred == hipSuccess) t.deferred = q;
+  }
   return hipSuccess;
 }
 
@@ -1066,6 +1072,8 @@ pg_status pg_kernel_timing(int32_t enable) {
   Timing &t = timing();
   std::lock_guard<std::mutex> lock(t.mu);
   hipError_t e = drain(t, true);
+  if (e == hipSuccess) e = t.deferred;
+  t.deferred = hipSuccess;
   for (int i = 0; i < PG_KERNEL_COUNT; ++i) {
     t.launches[i] = 0;
     t.total_ms[i] = 0.0;
@@ -1080,6 +1088,8 @@ pg_status pg_kernel_times(int32_t kernel_id, int64_t *launches, double *total_ms
   Timing &t = timing();
   std::lock_guard<std::mutex> lock(t.mu);
   hipError_t e = drain(t, true);
+  if (e == hipSuccess) e = t.deferred;
+  t.deferred = hipSuccess;
   *launches = t.launches[kernel_id];
   *total_ms = t.total_ms[kernel_id];
   return hip_status(e, "pg_kernel_times");
