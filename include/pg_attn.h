@@ -39,8 +39,8 @@
  *     pg_attn_bwd_noalloc's device scratch array, PG_NOALLOC_SCRATCH_BYTES per
  *     device, placed by the HIP runtime when the library's code objects are
  *     loaded on that device; (3) the kernel timing table and its event pool
- *     (pg_kernel_timing); (4) the thread-local message of pg_last_error.  None of it carries results from one call to
- *     the next.
+ *     (pg_kernel_timing); (4) the thread-local message of pg_last_error.
+ *     None of it carries results from one call to the next.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Kernels are
  *     enqueued on it; the call returns before they finish.
  *   - Results are bitwise reproducible for the same inputs, descriptor and
@@ -359,7 +359,10 @@ pg_status pg_logprob_bwd(const pg_desc *d, const void *hidden, const void *weigh
  * pg_kernel_timing(0) disables.  pg_kernel_times waits for the recorded events
  * and returns the number of launches and their total duration in milliseconds
  * for one kernel id (PG_KERNEL_*); it fails with PG_ERR_INVALID_ARG for an
- * unknown id.  pg_kernel_name returns the kernel's name, or NULL.  Not
+ * unknown id.  A HIP error met while folding the events of earlier launches
+ * (an earlier kernel's fault, for instance) is returned as PG_ERR_HIP by the
+ * next pg_kernel_timing or pg_kernel_times call, not by the launching call.
+ * pg_kernel_name returns the kernel's name, or NULL.  Not
  * thread-safe with respect to concurrent enabling/reading.  The PG_F32
  * backward is one launch doing both the dK/dV and the dQ work, counted under
  * PG_KERNEL_BWD_DKDV; PG_KERNEL_BWD_PRE counts nothing (both backward paths
