@@ -142,6 +142,29 @@ def test_head_configurations(name, groups, hq, hkv, d, dtype):
     _full_check(scaled_down(name, groups, dtype, hq, hkv, d, seed=zlib.crc32(name.encode()) % 1000))
 
 
+def _many_tiny_groups():
+    rng = np.random.default_rng(77)
+    return [(int(rng.integers(0, 6)), [int(r) for r in rng.integers(0, 6, size=int(rng.integers(1, 4)))])
+            for _ in range(300)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_long_response_short_prefix(dtype):
+    """One 6000-row response behind a 64-row prefix: the own-segment part of
+    every walk dominates (forward and dQ rows stream up to 94 response key
+    chunks; dK/dV response key tiles walk thousands of rows)."""
+    w = scaled_down("long_response", [(64, [6000, 3])], dtype, 8, 2, 128, seed=41)
+    _full_check(w, kv_heads=[1])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_many_tiny_groups(dtype):
+    """300 groups of 0-5 prefix rows and 1-3 responses of 0-5 rows: tiles
+    and key tiles far smaller than a workgroup's rows, many group borders."""
+    w = scaled_down("many_tiny_groups", _many_tiny_groups(), dtype, 4, 2, 64, seed=42)
+    _full_check(w)
+
+
 def _random_layout(seed):
     """A seeded random varlen batch: 1-3 groups, prefixes 0-400 rows, 1-12
     responses of 0-200 rows each, a random head configuration and d."""
